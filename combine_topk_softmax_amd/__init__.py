@@ -1,0 +1,230 @@
+"""Fused MoE layer for AMD Instinct MI355X (gfx950): Python binding.
+
+A thin ctypes layer over ``libmoe_gfx950.so`` (see ``include/moe.h``): it only
+marshals torch tensors, streams and events into the C ABI.  Every step of the
+layer runs in the library's HIP kernels; there is no fallback of any kind, and
+importing the binding without the built library raises.
+
+Build the library in-tree with ``python -m combine_topk_softmax_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_gfx950.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+FORMAT_STANDARD, FORMAT_BATCHED_EXPERTS = 0, 1
+DTYPE_F32, DTYPE_BF16, DTYPE_FP8_E4M3 = 0, 1, 2
+QUANT_NONE, QUANT_FP8_TOKEN_GROUP_128 = 0, 1
+SCORING_SOFTMAX, SCORING_SIGMOID = 0, 1
+DEVICE_BAD_EXPERT_ID, DEVICE_CAPACITY_OVERFLOW = 1, 2
+NUM_STAGE_EVENTS = 6
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_str(status)} ({status})")
+        self.status = status
+
+
+class Problem(C.Structure):
+    _fields_ = [
+        ("E", C.c_int64), ("M", C.c_int64), ("N", C.c_int64), ("K", C.c_int64),
+        ("topk", C.c_int64), ("max_tokens_per_expert", C.c_int64), ("align", C.c_int64),
+        ("shared_N", C.c_int64),
+        ("format", C.c_int32), ("act_dtype", C.c_int32), ("w_dtype", C.c_int32),
+        ("act_quant", C.c_int32), ("scoring", C.c_int32), ("renormalize", C.c_int32),
+        ("activation", C.c_int32), ("apply_router_weight_on_input", C.c_int32),
+        ("expert_map", C.c_void_p),
+    ]
+
+
+class Weights(C.Structure):
+    _fields_ = [("w1", C.c_void_p), ("w1_scale", C.c_void_p), ("w2", C.c_void_p), ("w2_scale", C.c_void_p)]
+
+
+class Shared(C.Structure):
+    _fields_ = [("w1", C.c_void_p), ("w2", C.c_void_p), ("out", C.c_void_p), ("aux_stream", C.c_void_p),
+                ("input_ready", C.c_void_p), ("output_ready", C.c_void_p)]
+
+
+class StageEvents(C.Structure):
+    _fields_ = [("ev", C.c_void_p * NUM_STAGE_EVENTS)]
+
+
+class WsLayout(C.Structure):
+    _fields_ = [(n, C.c_size_t) for n in (
+        "total_bytes", "status", "counts", "offsets", "chunk_hist", "tiles", "perm", "inv", "act",
+        "act_q", "act_scale", "topk_weights", "topk_ids", "a_q", "a_scale", "fused_out", "shared_act")]
+    _fields_ += [(n, C.c_int64) for n in ("perm_len", "n_chunks", "chunk", "max_tiles", "tile_rows", "act_rows")]
+
+
+EXPORTS = ("moe_status_str", "moe_version", "moe_validate", "moe_workspace_size", "moe_workspace_layout",
+           "moe_route", "moe_prepare", "moe_experts", "moe_finalize", "moe_shared_expert", "moe_forward")
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m combine_topk_softmax_amd.build`")
+    L = C.CDLL(path)
+    vp, P = C.c_void_p, C.POINTER
+    L.moe_status_str.restype = C.c_char_p
+    L.moe_status_str.argtypes = [C.c_int]
+    L.moe_version.restype = C.c_int
+    for name, args in {
+        "moe_validate": [P(Problem)],
+        "moe_workspace_size": [P(Problem), P(C.c_size_t)],
+        "moe_workspace_layout": [P(Problem), P(WsLayout)],
+        "moe_route": [P(Problem), vp, vp, vp, vp],
+        "moe_prepare": [P(Problem), vp, vp, vp, vp, vp, vp, C.c_size_t, vp],
+        "moe_experts": [P(Problem), vp, vp, P(Weights), vp, vp, vp, C.c_size_t, vp],
+        "moe_finalize": [P(Problem), vp, vp, vp, vp, C.c_size_t, vp],
+        "moe_shared_expert": [P(Problem), vp, vp, vp, vp, vp, C.c_size_t, vp],
+        "moe_forward": [P(Problem), vp, vp, P(Weights), vp, P(Shared), vp, C.c_size_t, vp, P(StageEvents)],
+    }.items():
+        f = getattr(L, name)
+        f.restype = C.c_int
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return load_library().moe_status_str(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors passed to the HIP library must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the HIP library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _ws(ws: torch.Tensor):
+    return _ptr(ws), ws.numel() * ws.element_size()
+
+
+def make_problem(E, M, N, K, topk, *, format=FORMAT_STANDARD, act_dtype=DTYPE_BF16, w_dtype=DTYPE_BF16,
+                 act_quant=QUANT_NONE, scoring=SCORING_SOFTMAX, renormalize=False,
+                 max_tokens_per_expert=0, align=0, shared_N=0) -> Problem:
+    return Problem(E=E, M=M, N=N, K=K, topk=topk, max_tokens_per_expert=max_tokens_per_expert, align=align,
+                   shared_N=shared_N, format=format, act_dtype=act_dtype, w_dtype=w_dtype,
+                   act_quant=act_quant, scoring=scoring, renormalize=int(renormalize), activation=0,
+                   apply_router_weight_on_input=0, expert_map=None)
+
+
+def validate(p: Problem) -> int:
+    return load_library().moe_validate(C.byref(p))
+
+
+def workspace_size(p: Problem) -> int:
+    n = C.c_size_t()
+    _check(load_library().moe_workspace_size(C.byref(p), C.byref(n)), "moe_workspace_size")
+    return n.value
+
+
+def workspace_layout(p: Problem) -> WsLayout:
+    L = WsLayout()
+    _check(load_library().moe_workspace_layout(C.byref(p), C.byref(L)), "moe_workspace_layout")
+    return L
+
+
+def empty_workspace(p: Problem, device="cuda") -> torch.Tensor:
+    return torch.empty(workspace_size(p), dtype=torch.uint8, device=device)
+
+
+def moe_route(p: Problem, logits, topk_weights, topk_ids, stream=None):
+    _check(load_library().moe_route(C.byref(p), _ptr(logits), _ptr(topk_weights), _ptr(topk_ids),
+                                    _stream(stream)), "moe_route")
+
+
+def moe_prepare(p: Problem, x, topk_ids, a_out, a_scale_out, expert_num_tokens, workspace, stream=None):
+    wp, wn = _ws(workspace)
+    _check(load_library().moe_prepare(C.byref(p), _ptr(x), _ptr(topk_ids), _ptr(a_out), _ptr(a_scale_out),
+                                      _ptr(expert_num_tokens), wp, wn, _stream(stream)), "moe_prepare")
+
+
+def _weights(w1, w1_scale, w2, w2_scale) -> Weights:
+    return Weights(_ptr(w1), _ptr(w1_scale), _ptr(w2), _ptr(w2_scale))
+
+
+def moe_experts(p: Problem, a, a_scale, w1, w1_scale, w2, w2_scale, expert_num_tokens, fused_out, workspace,
+                stream=None):
+    wp, wn = _ws(workspace)
+    w = _weights(w1, w1_scale, w2, w2_scale)
+    _check(load_library().moe_experts(C.byref(p), _ptr(a), _ptr(a_scale), C.byref(w), _ptr(expert_num_tokens),
+                                      _ptr(fused_out), wp, wn, _stream(stream)), "moe_experts")
+
+
+def moe_finalize(p: Problem, fused_out, topk_weights, out, workspace, stream=None):
+    wp, wn = _ws(workspace)
+    _check(load_library().moe_finalize(C.byref(p), _ptr(fused_out), _ptr(topk_weights), _ptr(out), wp, wn,
+                                       _stream(stream)), "moe_finalize")
+
+
+def moe_shared_expert(p: Problem, x, w1, w2, out, workspace, stream=None):
+    wp, wn = _ws(workspace)
+    _check(load_library().moe_shared_expert(C.byref(p), _ptr(x), _ptr(w1), _ptr(w2), _ptr(out), wp, wn,
+                                            _stream(stream)), "moe_shared_expert")
+
+
+def _event_handle(ev: torch.cuda.Event) -> int:
+    if ev.cuda_event == 0:            # torch creates events lazily
+        ev.record()
+    return ev.cuda_event
+
+
+class SharedExpertStreams:
+    """The aux stream and the two events the shared expert overlaps with."""
+
+    def __init__(self, device=None):
+        self.stream = torch.cuda.Stream(device=device)
+        self.input_ready = torch.cuda.Event()
+        self.output_ready = torch.cuda.Event()
+
+
+def moe_forward(p: Problem, logits, x, w1, w1_scale, w2, w2_scale, out, workspace, stream=None,
+                shared=None, shared_streams: Optional[SharedExpertStreams] = None, events=None):
+    """shared = (w1s, w2s, shared_out); events = list of torch.cuda.Event (timing) or None."""
+    L = load_library()
+    wp, wn = _ws(workspace)
+    w = _weights(w1, w1_scale, w2, w2_scale)
+    sh = None
+    if shared is not None:
+        if shared_streams is None:
+            raise ValueError("a shared expert needs SharedExpertStreams")
+        w1s, w2s, sout = shared
+        sh = Shared(_ptr(w1s), _ptr(w2s), _ptr(sout), shared_streams.stream.cuda_stream,
+                    _event_handle(shared_streams.input_ready), _event_handle(shared_streams.output_ready))
+    ev = None
+    if events is not None:
+        ev = StageEvents()
+        for i, e in enumerate(events[:NUM_STAGE_EVENTS]):
+            ev.ev[i] = _event_handle(e) if e is not None else None
+    _check(L.moe_forward(C.byref(p), _ptr(logits), _ptr(x), C.byref(w), _ptr(out),
+                         C.byref(sh) if sh is not None else None, wp, wn, _stream(stream),
+                         C.byref(ev) if ev is not None else None), "moe_forward")

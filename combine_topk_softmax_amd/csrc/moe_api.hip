@@ -1,0 +1,396 @@
+// C ABI of the fused MoE layer: host-side validation, workspace planning and
+// launch sequencing on the caller's streams.  No allocation, no host
+// synchronisation, no device reads: everything is stream-ordered and can be
+// captured into a hipGraph.
+#include <string.h>
+
+#include <algorithm>
+
+#include "moe_device.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int64_t kAlign = 256;
+constexpr int64_t kMaxExperts = 1024;
+constexpr int64_t kInt32Max = 2147483647;
+
+int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+int64_t act_elem_bytes(int32_t dt) { return dt == MOE_DTYPE_F32 ? 4 : 2; }
+
+bool fp8_path(const moe_problem &p) { return p.w_dtype == MOE_DTYPE_FP8_E4M3; }
+
+// Checks of _moe_problem_size, the activation's 2:1 width rule,
+// the format agreement of FusedMoEModularKernel.__init__ and the
+// unsupported-activation error (all on the modular_kernel.py page), plus
+// this library's tile and index limits.
+moe_status validate(const moe_problem *pp) {
+  if (!pp) return MOE_ERR_INVALID_ARG;
+  const moe_problem &p = *pp;
+  if (p.E < 1 || p.M < 0 || p.N < 2 || p.K < 1 || p.topk < 1) return MOE_ERR_INVALID_ARG;
+  if (p.N % 2 != 0 || p.topk > p.E) return MOE_ERR_INVALID_ARG;
+  if (p.format != MOE_FORMAT_STANDARD && p.format != MOE_FORMAT_BATCHED_EXPERTS) return MOE_ERR_INVALID_ARG;
+  if (p.scoring != MOE_SCORING_SOFTMAX && p.scoring != MOE_SCORING_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (p.align < 0 || p.shared_N < 0) return MOE_ERR_INVALID_ARG;
+  if (p.format == MOE_FORMAT_BATCHED_EXPERTS && p.max_tokens_per_expert < 1) return MOE_ERR_INVALID_ARG;
+  if (p.act_dtype != MOE_DTYPE_F32 && p.act_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
+  if (p.w_dtype != MOE_DTYPE_F32 && p.w_dtype != MOE_DTYPE_BF16 && p.w_dtype != MOE_DTYPE_FP8_E4M3)
+    return MOE_ERR_INVALID_ARG;
+  if (p.act_quant != MOE_QUANT_NONE && p.act_quant != MOE_QUANT_FP8_TOKEN_GROUP_128) return MOE_ERR_INVALID_ARG;
+  if (p.activation != MOE_ACTIVATION_SILU) return MOE_ERR_UNSUPPORTED;
+  if (p.apply_router_weight_on_input != 0 || p.expert_map != nullptr) return MOE_ERR_UNSUPPORTED;
+  if (p.E > kMaxExperts || p.topk > 64) return MOE_ERR_UNSUPPORTED;
+  const int64_t I = p.N / 2;
+  if (p.K % 128 != 0 || I % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  // dtype combinations: fp32 x fp32, bf16 x bf16, fp8-quantised x fp8
+  if (fp8_path(p)) {
+    if (p.act_quant != MOE_QUANT_FP8_TOKEN_GROUP_128 || I % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  } else {
+    if (p.act_quant != MOE_QUANT_NONE || p.w_dtype != p.act_dtype) return MOE_ERR_UNSUPPORTED;
+  }
+  if (p.shared_N > 0 && (p.shared_N % 128 != 0 || fp8_path(p))) return MOE_ERR_UNSUPPORTED;
+  const int64_t align = p.align > 0 ? p.align : 1;
+  if (align > 4096) return MOE_ERR_UNSUPPORTED;
+  const int64_t pairs = p.M * p.topk;
+  if (pairs + p.E * (align - 1) > kInt32Max / 2) return MOE_ERR_UNSUPPORTED;
+  if (p.format == MOE_FORMAT_BATCHED_EXPERTS && p.E * p.max_tokens_per_expert > kInt32Max / 2)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+void layout(const moe_problem &p, moe_ws_layout &L) {
+  memset(&L, 0, sizeof(L));
+  const int64_t n = p.M * p.topk;
+  const int64_t E = p.E, I = p.N / 2;
+  const bool standard = p.format == MOE_FORMAT_STANDARD;
+  const int64_t align = p.align > 0 ? p.align : 1;
+  const int64_t cap = standard ? 0 : p.max_tokens_per_expert;
+  const int64_t eb = act_elem_bytes(p.act_dtype);
+  const bool fp8 = fp8_path(p);
+
+  L.perm_len = standard ? n + E * (align - 1) : 0;
+  L.chunk = std::max<int64_t>(1024, round_up((n + 63) / 64, 256));
+  L.n_chunks = std::max<int64_t>(1, (n + L.chunk - 1) / L.chunk);
+  L.tile_rows = kTileRows;
+  const int64_t tiled_rows = standard ? n : std::min(n, E * cap);
+  L.max_tiles = std::max<int64_t>(1, (tiled_rows + E * (kTileRows - 1)) / kTileRows);
+  L.act_rows = standard ? L.perm_len : E * cap;
+
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    size_t at = (size_t)off;
+    off = round_up(off + std::max<int64_t>(bytes, 0), kAlign);
+    return at;
+  };
+  L.status = take(4);
+  L.counts = take(4 * E);
+  L.offsets = take(4 * (E + 1));
+  L.chunk_hist = take(4 * L.n_chunks * E);
+  L.tiles = take(4 * (L.max_tiles * 4 + 1));
+  L.perm = take(4 * L.perm_len);
+  L.inv = take(4 * n);
+  L.act = take(L.act_rows * I * (fp8 ? 4 : eb));
+  L.act_q = take(fp8 ? L.act_rows * I : 0);
+  L.act_scale = take(fp8 ? L.act_rows * (I / 128) * 4 : 0);
+  L.topk_weights = take(4 * n);
+  L.topk_ids = take(4 * n);
+  const int64_t a_rows = standard ? p.M : E * cap;
+  const bool need_a = !standard || fp8;
+  L.a_q = take(need_a ? a_rows * p.K * (fp8 ? 1 : eb) : 0);
+  L.a_scale = take(need_a && fp8 ? a_rows * (p.K / 128) * 4 : 0);
+  L.fused_out = take((standard ? n : E * cap) * p.K * eb);
+  L.shared_act = take(p.shared_N > 0 ? p.M * (p.shared_N / 2) * eb : 0);
+  L.total_bytes = (size_t)off;
+}
+
+template <typename T>
+T *at(void *ws, size_t off) {
+  return reinterpret_cast<T *>(reinterpret_cast<uint8_t *>(ws) + off);
+}
+
+#define MOE_HIP(call)                      \
+  do {                                     \
+    if ((call) != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+
+moe_status check_ws(const moe_problem &p, void *ws, size_t ws_bytes, moe_ws_layout &L) {
+  layout(p, L);
+  if (!ws) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < L.total_bytes) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+void record(const moe_stage_events *ev, int i, hipStream_t s) {
+  if (ev && ev->ev[i]) (void)hipEventRecord(ev->ev[i], s);
+}
+
+moe_status do_prepare(const moe_problem &p, const void *x, const int32_t *ids, void *a_out,
+                      float *a_scale_out, int32_t *expert_num_tokens, void *ws,
+                      const moe_ws_layout &L, hipStream_t s) {
+  DispatchBufs b;
+  b.status = at<int32_t>(ws, L.status);
+  b.counts = at<int32_t>(ws, L.counts);
+  b.offsets = at<int32_t>(ws, L.offsets);
+  b.chunk_hist = at<int32_t>(ws, L.chunk_hist);
+  b.perm = at<int32_t>(ws, L.perm);
+  b.inv = at<int32_t>(ws, L.inv);
+  b.perm_len = L.perm_len;
+  b.n_chunks = L.n_chunks;
+  b.chunk = L.chunk;
+  MOE_HIP(launch_count_and_permute(p, ids, expert_num_tokens, b, s));
+  const bool batched = p.format == MOE_FORMAT_BATCHED_EXPERTS;
+  if (batched || p.act_quant == MOE_QUANT_FP8_TOKEN_GROUP_128)
+    MOE_HIP(launch_dispatch_rows(p, x, b.inv, a_out, a_scale_out, batched, s));
+  return MOE_OK;
+}
+
+moe_status do_experts(const moe_problem &p, const void *a, const float *a_scale, const moe_weights &w,
+                      const int32_t *counts, void *fused_out, void *ws, const moe_ws_layout &L,
+                      hipStream_t s, const moe_stage_events *ev) {
+  const bool standard = p.format == MOE_FORMAT_STANDARD;
+  const bool fp8 = fp8_path(p);
+  const int64_t I = p.N / 2;
+  int32_t *tiles = at<int32_t>(ws, L.tiles);
+  int32_t *status = at<int32_t>(ws, L.status);
+  int32_t *perm = standard ? at<int32_t>(ws, L.perm) : nullptr;
+  MOE_HIP(launch_plan_tiles(p, counts, at<int32_t>(ws, L.offsets), L.perm_len, (int)L.tile_rows,
+                            (int)L.max_tiles, tiles, status, s));
+  record(ev, 2, s);
+  GemmTiles gt;
+  gt.tiles = tiles;
+  gt.tile_count = tiles + L.max_tiles * 4;
+  gt.max_tiles = (int)L.max_tiles;
+  gt.dense_rows = 0;
+
+  GemmParams g1;
+  memset(&g1, 0, sizeof(g1));
+  g1.a = a;
+  g1.a_scale = a_scale;
+  g1.perm = perm;
+  g1.topk = (int)p.topk;
+  g1.n_pairs = (int)(p.M * p.topk);
+  g1.w = w.w1;
+  g1.w_scale = w.w1_scale;
+  g1.Nw = p.N;
+  g1.Kred = p.K;
+  g1.out = at<void>(ws, L.act);
+  g1.ldo = I;
+  g1.half_n = I;
+  g1.t = gt;
+  MOE_HIP(launch_grouped_gemm(p.w_dtype, fp8 ? MOE_DTYPE_F32 : p.act_dtype, kGemmGatedAct, g1,
+                              (int)(I / 64), s));
+  record(ev, 3, s);
+  if (fp8)
+    MOE_HIP(launch_quant_rows(at<float>(ws, L.act), tiles, (int)L.max_tiles, I, at<uint8_t>(ws, L.act_q),
+                              at<float>(ws, L.act_scale), s));
+
+  GemmParams g2;
+  memset(&g2, 0, sizeof(g2));
+  g2.a = fp8 ? at<void>(ws, L.act_q) : at<void>(ws, L.act);
+  g2.a_scale = fp8 ? at<float>(ws, L.act_scale) : nullptr;
+  g2.perm = nullptr;
+  g2.topk = (int)p.topk;
+  g2.n_pairs = (int)(p.M * p.topk);
+  g2.w = w.w2;
+  g2.w_scale = w.w2_scale;
+  g2.Nw = p.K;
+  g2.Kred = I;
+  g2.out = fused_out;
+  g2.ldo = p.K;
+  g2.out_perm = perm;
+  g2.half_n = 0;
+  g2.t = gt;
+  MOE_HIP(launch_grouped_gemm(p.w_dtype, p.act_dtype, kGemmDown, g2, (int)(p.K / 128), s));
+  record(ev, 4, s);
+  return MOE_OK;
+}
+
+moe_status do_shared(const moe_problem &p, const void *x, const void *w1, const void *w2, void *out,
+                     void *ws, const moe_ws_layout &L, hipStream_t s) {
+  const int64_t Is = p.shared_N / 2;
+  GemmTiles gt;
+  gt.tiles = nullptr;
+  gt.tile_count = nullptr;
+  gt.max_tiles = 0;
+  gt.dense_rows = (int)p.M;
+  GemmParams g1;
+  memset(&g1, 0, sizeof(g1));
+  g1.a = x;
+  g1.topk = 1;
+  g1.n_pairs = (int)p.M;
+  g1.w = w1;
+  g1.Nw = p.shared_N;
+  g1.Kred = p.K;
+  g1.out = at<void>(ws, L.shared_act);
+  g1.ldo = Is;
+  g1.half_n = Is;
+  g1.t = gt;
+  MOE_HIP(launch_grouped_gemm(p.act_dtype, p.act_dtype, kGemmGatedAct, g1, (int)(Is / 64), s));
+  GemmParams g2;
+  memset(&g2, 0, sizeof(g2));
+  g2.a = at<void>(ws, L.shared_act);
+  g2.topk = 1;
+  g2.n_pairs = (int)p.M;
+  g2.w = w2;
+  g2.Nw = p.K;
+  g2.Kred = Is;
+  g2.out = out;
+  g2.ldo = p.K;
+  g2.t = gt;
+  MOE_HIP(launch_grouped_gemm(p.act_dtype, p.act_dtype, kGemmDown, g2, (int)(p.K / 128), s));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+int moe_version(void) { return 1; }
+
+moe_status moe_validate(const moe_problem *p) { return validate(p); }
+
+moe_status moe_workspace_layout(const moe_problem *p, moe_ws_layout *out) {
+  moe_status st = validate(p);
+  if (st != MOE_OK) return st;
+  if (!out) return MOE_ERR_INVALID_ARG;
+  layout(*p, *out);
+  return MOE_OK;
+}
+
+moe_status moe_workspace_size(const moe_problem *p, size_t *bytes) {
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  moe_ws_layout L;
+  moe_status st = moe_workspace_layout(p, &L);
+  if (st == MOE_OK) *bytes = L.total_bytes;
+  return st;
+}
+
+moe_status moe_route(const moe_problem *p, const float *logits, float *topk_weights,
+                     int32_t *topk_ids, hipStream_t stream) {
+  moe_status st = validate(p);
+  if (st != MOE_OK) return st;
+  if (p->M == 0) return MOE_OK;
+  if (!logits || !topk_weights || !topk_ids) return MOE_ERR_INVALID_ARG;
+  MOE_HIP(launch_route(*p, logits, topk_weights, topk_ids, stream));
+  return MOE_OK;
+}
+
+moe_status moe_prepare(const moe_problem *p, const void *x, const int32_t *topk_ids, void *a_out,
+                       float *a_scale_out, int32_t *expert_num_tokens, void *workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  moe_status st = validate(p);
+  if (st != MOE_OK) return st;
+  if (p->M == 0) return MOE_OK;
+  moe_ws_layout L;
+  if ((st = check_ws(*p, workspace, workspace_bytes, L)) != MOE_OK) return st;
+  if (!x || !topk_ids || !expert_num_tokens) return MOE_ERR_INVALID_ARG;
+  const bool quant = p->act_quant == MOE_QUANT_FP8_TOKEN_GROUP_128;
+  const bool batched = p->format == MOE_FORMAT_BATCHED_EXPERTS;
+  if ((batched || quant) && !a_out) return MOE_ERR_INVALID_ARG;
+  if (quant && !a_scale_out) return MOE_ERR_INVALID_ARG;
+  if (!batched && !quant && (a_out || a_scale_out)) return MOE_ERR_INVALID_ARG;
+  return do_prepare(*p, x, topk_ids, a_out, a_scale_out, expert_num_tokens, workspace, L, stream);
+}
+
+moe_status moe_experts(const moe_problem *p, const void *a, const float *a_scale,
+                       const moe_weights *w, const int32_t *expert_num_tokens, void *fused_out,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  moe_status st = validate(p);
+  if (st != MOE_OK) return st;
+  if (p->M == 0) return MOE_OK;
+  moe_ws_layout L;
+  if ((st = check_ws(*p, workspace, workspace_bytes, L)) != MOE_OK) return st;
+  if (!a || !w || !w->w1 || !w->w2 || !expert_num_tokens || !fused_out) return MOE_ERR_INVALID_ARG;
+  if (fp8_path(*p) && (!a_scale || !w->w1_scale || !w->w2_scale)) return MOE_ERR_INVALID_ARG;
+  return do_experts(*p, a, a_scale, *w, expert_num_tokens, fused_out, workspace, L, stream, nullptr);
+}
+
+moe_status moe_finalize(const moe_problem *p, const void *fused_out, const float *topk_weights,
+                        void *out, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  moe_status st = validate(p);
+  if (st != MOE_OK) return st;
+  if (p->M == 0) return MOE_OK;
+  moe_ws_layout L;
+  if ((st = check_ws(*p, workspace, workspace_bytes, L)) != MOE_OK) return st;
+  if (!fused_out || !topk_weights || !out) return MOE_ERR_INVALID_ARG;
+  const int32_t *inv = p->format == MOE_FORMAT_BATCHED_EXPERTS ? at<int32_t>(workspace, L.inv) : nullptr;
+  MOE_HIP(launch_combine(*p, fused_out, topk_weights, inv, out, stream));
+  return MOE_OK;
+}
+
+moe_status moe_shared_expert(const moe_problem *p, const void *x, const void *w1, const void *w2,
+                             void *out, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  moe_status st = validate(p);
+  if (st != MOE_OK) return st;
+  if (p->shared_N <= 0) return MOE_ERR_INVALID_ARG;
+  if (p->M == 0) return MOE_OK;
+  moe_ws_layout L;
+  if ((st = check_ws(*p, workspace, workspace_bytes, L)) != MOE_OK) return st;
+  if (!x || !w1 || !w2 || !out) return MOE_ERR_INVALID_ARG;
+  return do_shared(*p, x, w1, w2, out, workspace, L, stream);
+}
+
+moe_status moe_forward(const moe_problem *p, const float *logits, const void *x,
+                       const moe_weights *w, void *out, const moe_shared *shared,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream,
+                       const moe_stage_events *events) {
+  moe_status st = validate(p);
+  if (st != MOE_OK) return st;
+  if ((shared != nullptr) != (p->shared_N > 0)) return MOE_ERR_INVALID_ARG;
+  if (p->M == 0) return MOE_OK;
+  moe_ws_layout L;
+  if ((st = check_ws(*p, workspace, workspace_bytes, L)) != MOE_OK) return st;
+  if (!logits || !x || !w || !w->w1 || !w->w2 || !out) return MOE_ERR_INVALID_ARG;
+  if (fp8_path(*p) && (!w->w1_scale || !w->w2_scale)) return MOE_ERR_INVALID_ARG;
+  if (shared) {
+    if (!shared->w1 || !shared->w2 || !shared->out || !shared->aux_stream || !shared->input_ready ||
+        !shared->output_ready)
+      return MOE_ERR_INVALID_ARG;
+    if (out == x || shared->out == x) return MOE_ERR_INVALID_ARG;
+  }
+  record(events, 0, stream);
+  if (shared) {
+    // Shared expert on the aux stream, overlapping the routed path.
+    MOE_HIP(hipEventRecord(shared->input_ready, stream));
+    MOE_HIP(hipStreamWaitEvent(shared->aux_stream, shared->input_ready, 0));
+    if ((st = do_shared(*p, x, shared->w1, shared->w2, shared->out, workspace, L, shared->aux_stream)) != MOE_OK)
+      return st;
+    MOE_HIP(hipEventRecord(shared->output_ready, shared->aux_stream));
+  }
+  float *tw = at<float>(workspace, L.topk_weights);
+  int32_t *ti = at<int32_t>(workspace, L.topk_ids);
+  MOE_HIP(launch_route(*p, logits, tw, ti, stream));
+  record(events, 1, stream);
+
+  const bool standard = p->format == MOE_FORMAT_STANDARD;
+  const bool quant = p->act_quant == MOE_QUANT_FP8_TOKEN_GROUP_128;
+  void *a_q = (!standard || quant) ? at<void>(workspace, L.a_q) : nullptr;
+  float *a_s = quant ? at<float>(workspace, L.a_scale) : nullptr;
+  int32_t *counts = at<int32_t>(workspace, L.counts);
+  if ((st = do_prepare(*p, x, ti, a_q, a_s, counts, workspace, L, stream)) != MOE_OK) return st;
+
+  void *fused = at<void>(workspace, L.fused_out);
+  if ((st = do_experts(*p, a_q ? a_q : x, a_s, *w, counts, fused, workspace, L, stream, events)) != MOE_OK)
+    return st;
+  const int32_t *inv = standard ? nullptr : at<int32_t>(workspace, L.inv);
+  MOE_HIP(launch_combine(*p, fused, tw, inv, out, stream));
+  record(events, 5, stream);
+  if (shared) MOE_HIP(hipStreamWaitEvent(stream, shared->output_ready, 0));
+  return MOE_OK;
+}
+
+}  // extern "C"

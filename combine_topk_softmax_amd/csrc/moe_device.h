@@ -1,0 +1,145 @@
+// Device helpers and internal launch interfaces of the gfx950 fused-MoE
+// library.  Everything here is CDNA4-specific: 64-lane wavefronts, MFMA
+// builtins, LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------- conversions
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float -> bfloat16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// float -> OCP e4m3fn code, round to nearest even.  The callers clamp to
+// [-448, 448] first; magnitudes >= 448 give 448.  Subnormals (|v| < 2^-6) are
+// multiples of 2^-9: scaling by 2^9 is exact and rint() rounds ties to even.
+// Normals keep 3 mantissa bits: adding 0x7ffff plus the kept LSB to the fp32
+// pattern rounds the 20 dropped bits to nearest even, a carry moving into the
+// exponent as it should.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t sign = (u >> 24) & 0x80u;
+  u &= 0x7fffffffu;
+  if (u >= 0x43e00000u) return sign | 0x7eu;          // >= 448
+  if (u < 0x3c800000u) {                              // < 2^-6
+    float t = __uint_as_float(u) * 512.0f;
+    return sign | (uint32_t)__builtin_rintf(t);
+  }
+  uint32_t r = u + 0x7ffffu + ((u >> 20) & 1u);
+  uint32_t code = (((r >> 23) - 120u) << 3) | ((r >> 20) & 7u);
+  return sign | (code > 0x7eu ? 0x7eu : code);
+}
+
+// One token-group-128 quantisation step: scale from the group's |max|, codes
+// of clamp(x / scale).  Both divisions are IEEE fp32 (hipcc's default).
+__device__ __forceinline__ float group_scale(float amax) { return fmaxf(amax, 1e-10f) / 448.0f; }
+
+__device__ __forceinline__ uint32_t quant_e4m3(float x, float scale) {
+  float t = x / scale;
+  t = fminf(fmaxf(t, -448.0f), 448.0f);
+  return f32_to_e4m3(t);
+}
+
+// ------------------------------------------------------------- wave utils
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  uint32_t lane = __lane_id();
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint32_t lo = __shfl_xor((uint32_t)v, o, 64);
+    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
+    uint64_t w = ((uint64_t)hi << 32) | lo;
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// ------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error; shapes are validated by the
+// C ABI before these are called.
+
+struct GemmTiles {
+  const int32_t *tiles;       // [max_tiles][4] = {expert, seg_base, row0, nrows}
+  const int32_t *tile_count;  // device count of valid tiles
+  int max_tiles;
+  int dense_rows;             // > 0: dense (one expert, rows 0..dense_rows)
+};
+
+enum GemmKind { kGemmGatedAct = 0, kGemmDown = 1 };
+
+struct GemmParams {
+  // A operand: activation rows
+  const void *a;
+  const float *a_scale;       // fp8: [rows, Kred/128]
+  const int32_t *perm;        // slot -> pair (gather by perm[slot] / topk); NULL: row = slot
+  int topk;
+  int n_pairs;                // bound of perm values (M*topk)
+  // B operand: weights [E, Nw, Kred]
+  const void *w;
+  const float *w_scale;       // fp8: [E, Nw/128, Kred/128]
+  int64_t Nw;
+  int64_t Kred;
+  // output
+  void *out;
+  int64_t ldo;
+  const int32_t *out_perm;    // down GEMM: slot -> output row; NULL: row = slot
+  int64_t half_n;             // gated: I (up rows start here)
+  GemmTiles t;
+};
+
+hipError_t launch_route(const moe_problem &p, const float *logits, float *w, int32_t *ids,
+                        hipStream_t s);
+
+struct DispatchBufs {
+  int32_t *status, *counts, *offsets, *chunk_hist, *perm, *inv;
+  int64_t perm_len, n_chunks, chunk;
+};
+
+hipError_t launch_count_and_permute(const moe_problem &p, const int32_t *ids, int32_t *expert_num_tokens,
+                                    const DispatchBufs &b, hipStream_t s);
+hipError_t launch_dispatch_rows(const moe_problem &p, const void *x, const int32_t *inv, void *a_out,
+                                float *a_scale_out, bool batched, hipStream_t s);
+hipError_t launch_plan_tiles(const moe_problem &p, const int32_t *counts, const int32_t *offsets,
+                             int64_t perm_len, int tile_rows, int max_tiles, int32_t *tiles,
+                             int32_t *status, hipStream_t s);
+hipError_t launch_quant_rows(const float *in, const int32_t *tiles, int max_tiles, int64_t cols,
+                             uint8_t *q, float *scale, hipStream_t s);
+hipError_t launch_grouped_gemm(int w_dtype, int out_dtype, GemmKind kind, const GemmParams &g,
+                               int n_tiles, hipStream_t s);
+hipError_t launch_combine(const moe_problem &p, const void *fused_out, const float *topk_w,
+                          const int32_t *inv, void *out, hipStream_t s);
+
+constexpr int kTileRows = 128;   // grouped-GEMM rows per tile (BM)
+constexpr int kTileCols = 128;   // grouped-GEMM weight rows per tile (BN)
+
+}  // namespace moe

@@ -1,0 +1,161 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/moe.h declares, the ctypes structs match the C layout, and host-side
+validation returns the documented status codes (no kernel is launched)."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+import combine_topk_softmax_amd as moe
+from workloads import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:moe_status|const char \*|int)\s*\*?\s*(moe_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = moe.load_library()
+    names = _declared_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(moe.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True, text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}$", out, re.M), n
+
+
+def test_version_and_status_strings():
+    L = moe.load_library()
+    assert L.moe_version() == 1
+    assert moe.status_str(moe.MOE_OK) == "ok"
+    assert "workspace" in moe.status_str(moe.MOE_ERR_WORKSPACE)
+
+
+_LAYOUT_PROBE = r"""
+#include <stdio.h>
+#include <stddef.h>
+#include "moe.h"
+#define F(T, f) printf(#T "." #f " %zu\n", offsetof(T, f));
+int main(void) {
+  printf("moe_problem %zu\n", sizeof(moe_problem));
+  F(moe_problem, E) F(moe_problem, max_tokens_per_expert) F(moe_problem, shared_N) F(moe_problem, format)
+  F(moe_problem, apply_router_weight_on_input) F(moe_problem, expert_map)
+  printf("moe_weights %zu\n", sizeof(moe_weights));
+  printf("moe_shared %zu\n", sizeof(moe_shared));
+  F(moe_shared, output_ready)
+  printf("moe_stage_events %zu\n", sizeof(moe_stage_events));
+  printf("moe_ws_layout %zu\n", sizeof(moe_ws_layout));
+  F(moe_ws_layout, shared_act) F(moe_ws_layout, perm_len) F(moe_ws_layout, act_rows)
+  return 0;
+}
+"""
+
+
+def test_ctypes_structs_match_c_layout(tmp_path):
+    src = tmp_path / "probe.c"
+    src.write_text(_LAYOUT_PROBE)
+    exe = tmp_path / "probe"
+    subprocess.check_call(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                           "-I", "/opt/rocm/include", str(src), "-o", str(exe)])
+    got = dict(line.rsplit(" ", 1) for line in subprocess.check_output([str(exe)], text=True).splitlines())
+    py = {
+        "moe_problem": C.sizeof(moe.Problem), "moe_weights": C.sizeof(moe.Weights),
+        "moe_shared": C.sizeof(moe.Shared), "moe_stage_events": C.sizeof(moe.StageEvents),
+        "moe_ws_layout": C.sizeof(moe.WsLayout),
+    }
+    for k, v in py.items():
+        assert int(got[k]) == v, k
+    for key, val in got.items():
+        if "." in key:
+            struct, field = key.split(".")
+            cls = {"moe_problem": moe.Problem, "moe_shared": moe.Shared, "moe_ws_layout": moe.WsLayout}[struct]
+            assert getattr(cls, field).offset == int(val), key
+
+
+def _prob(wl):
+    return moe.make_problem(wl.E, wl.M, 2 * wl.I, wl.K, wl.topk, format=wl.format, act_dtype=wl.act_dtype,
+                            w_dtype=wl.w_dtype, act_quant=wl.act_quant, scoring=wl.scoring,
+                            renormalize=wl.renormalize, max_tokens_per_expert=wl.capacity,
+                            shared_N=2 * wl.shared_I)
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workloads_validate_and_layout(name):
+    wl = WORKLOADS[name]
+    p = _prob(wl)
+    assert moe.validate(p) == moe.MOE_OK
+    L = moe.workspace_layout(p)
+    assert L.total_bytes == moe.workspace_size(p)
+    n = wl.M * wl.topk
+    offs = sorted((getattr(L, f), f) for f, _ in moe.WsLayout._fields_[1:17])
+    assert all(o % 256 == 0 for o, _ in offs)
+    assert offs[-1][0] <= L.total_bytes
+    if wl.format == moe.FORMAT_STANDARD:
+        assert L.perm_len == n and L.act_rows == n
+    else:
+        assert L.act_rows == wl.E * wl.capacity
+    assert L.max_tiles >= -(-n // 128)
+    assert L.n_chunks * L.chunk >= n and L.n_chunks <= 64
+
+
+def test_validation_status_codes():
+    base = dict(E=8, M=16, N=256, K=256, topk=2)
+    ok = moe.make_problem(**base)
+    assert moe.validate(ok) == moe.MOE_OK
+    bad = [
+        (dict(base, topk=9), moe.MOE_ERR_INVALID_ARG),                 # topk > E
+        (dict(base, N=255), moe.MOE_ERR_INVALID_ARG),                  # odd N (activation halves it)
+        (dict(base, M=-1), moe.MOE_ERR_INVALID_ARG),
+        (dict(base, E=0), moe.MOE_ERR_INVALID_ARG),
+        (dict(base, K=200), moe.MOE_ERR_UNSUPPORTED),                  # K % 128
+        (dict(base, N=2 * 96), moe.MOE_ERR_UNSUPPORTED),               # I % 64
+        (dict(base, E=2048, topk=2), moe.MOE_ERR_UNSUPPORTED),
+    ]
+    for kw, code in bad:
+        assert moe.validate(moe.make_problem(**kw)) == code, kw
+    p = moe.make_problem(**base, format=moe.FORMAT_BATCHED_EXPERTS)          # capacity missing
+    assert moe.validate(p) == moe.MOE_ERR_INVALID_ARG
+    p = moe.make_problem(**base, w_dtype=moe.DTYPE_FP8_E4M3)                  # fp8 weights need fp8 acts
+    assert moe.validate(p) == moe.MOE_ERR_UNSUPPORTED
+    p = moe.make_problem(**base, act_dtype=moe.DTYPE_F32)                     # mixed f32 x bf16
+    assert moe.validate(p) == moe.MOE_ERR_UNSUPPORTED
+    p = moe.make_problem(**base)
+    p.activation = 1                                                          # only silu
+    assert moe.validate(p) == moe.MOE_ERR_UNSUPPORTED
+    p = moe.make_problem(**base)
+    p.apply_router_weight_on_input = 1
+    assert moe.validate(p) == moe.MOE_ERR_UNSUPPORTED
+    p = moe.make_problem(**base)
+    p.scoring = 7
+    assert moe.validate(p) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_host_errors_need_no_gpu():
+    """Calls that fail validation, or have M == 0, return before touching the device."""
+    L = moe.load_library()
+    p = moe.make_problem(E=8, M=16, N=256, K=256, topk=2)
+    ws_size = moe.workspace_size(p)
+    assert L.moe_route(C.byref(p), None, None, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_prepare(C.byref(p), None, None, None, None, None, None, 0, None) == moe.MOE_ERR_INVALID_ARG
+    fake = C.c_void_p(0x1000)
+    assert L.moe_prepare(C.byref(p), fake, fake, None, None, fake, fake, ws_size - 1, None) == moe.MOE_ERR_WORKSPACE
+    w = moe.Weights(None, None, None, None)
+    assert L.moe_experts(C.byref(p), fake, None, C.byref(w), fake, fake, fake, ws_size, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_finalize(C.byref(p), None, None, None, fake, ws_size, None) == moe.MOE_ERR_INVALID_ARG
+    # shared expert requested by the problem but not given
+    ps = moe.make_problem(E=8, M=16, N=256, K=256, topk=2, shared_N=256)
+    assert L.moe_forward(C.byref(ps), fake, fake, C.byref(w), fake, None, fake, 1 << 40, None, None) \
+        == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_shared_expert(C.byref(p), fake, fake, fake, fake, fake, ws_size, None) == moe.MOE_ERR_INVALID_ARG
+    # M == 0: nothing to do, nothing launched
+    p0 = moe.make_problem(E=8, M=0, N=256, K=256, topk=2)
+    assert L.moe_route(C.byref(p0), None, None, None, None) == moe.MOE_OK
+    assert L.moe_forward(C.byref(p0), None, None, None, None, None, None, 0, None, None) == moe.MOE_OK

@@ -1,0 +1,430 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on the GPU.
+
+Integer results (routing ids, counts, offsets, permutation, batched slots, fp8
+codes and scales of the first quantisation) must match bit for bit; float
+outputs within the bounds of tests/gpu_util.TOL.  Small shapes compare every
+element and span several tiles with ragged tails; full workload sizes compare
+every routing / permutation entry and a seeded sample of output rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import combine_topk_softmax_amd as moe
+import oracle
+from tests import gpu_util as U
+from workloads import (DTYPE_BF16, DTYPE_F32, DTYPE_FP8, FORMAT_BATCHED, FORMAT_STANDARD, QUANT_FP8_G128,
+                       SCORING_SIGMOID, WORKLOADS, make_inputs, make_logits, sample_tokens)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[gpu-test] {request.node.nodeid}", flush=True)
+    yield
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- router
+
+ROUTE_CASES = [(n, None) for n in WORKLOADS] + [
+    ("ties", dict(M=333, E=16, topk=4)), ("k_equals_E", dict(M=77, E=8, topk=8)),
+    ("E1", dict(M=5, E=1, topk=1)), ("E1024", dict(M=65, E=1024, topk=6)),
+    ("E200_sigmoid", dict(M=129, E=200, topk=8, scoring=SCORING_SIGMOID, renormalize=True)),
+]
+
+
+@pytest.mark.parametrize("name,over", ROUTE_CASES, ids=[c[0] for c in ROUTE_CASES])
+def test_route_parity(name, over):
+    wl = WORKLOADS.get(name, WORKLOADS["tiny_fp32"])
+    if over:
+        wl = wl.replace(**over)
+    logits = make_logits(wl, seed=11)
+    if name == "ties":
+        logits = torch.round(logits * 2) / 2       # many exact ties
+        logits[0, :] = -0.0
+        logits[0, 3] = 0.0
+    p = U.problem(wl)
+    lg = logits.cuda()
+    w = torch.empty(wl.M, wl.topk, device="cuda")
+    ids = torch.empty(wl.M, wl.topk, dtype=torch.int32, device="cuda")
+    moe.moe_route(p, lg, w, ids)
+    torch.cuda.synchronize()
+    rids, rw = oracle.route(logits, wl.topk, wl.scoring, wl.renormalize)
+    np.testing.assert_array_equal(ids.cpu().numpy(), rids)
+    np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=U.WEIGHT_RTOL, atol=1e-7)
+
+
+# ---------------------------------------------------------------- prepare
+
+def _ids_from_oracle(wl, seed=12):
+    ids, w = oracle.route(make_logits(wl, seed=seed), wl.topk, wl.scoring, wl.renormalize)
+    return ids, w
+
+
+STD_CASES = [("tiny_fp32", 1), ("mixtral_bf16", 1), ("dsv3_bf16", 1), ("skewed_bf16", 1),
+             ("tiny_fp32", 16), ("dsv3_bf16", 128), ("skewed_bf16", 7)]
+
+
+@pytest.mark.parametrize("name,align", STD_CASES)
+def test_prepare_standard_parity(name, align):
+    wl = WORKLOADS[name]
+    ids, _ = _ids_from_oracle(wl)
+    p = U.problem(wl, align=align)
+    L = moe.workspace_layout(p)
+    ws = moe.empty_workspace(p)
+    ws.fill_(0xAB)                                      # poison
+    counts = torch.empty(wl.E, dtype=torch.int32, device="cuda")
+    x = torch.zeros(wl.M, wl.K, dtype=U.torch_act_dtype(wl), device="cuda")
+    moe.moe_prepare(p, x, torch.from_numpy(ids).cuda(), None, None, counts, ws)
+    torch.cuda.synchronize()
+    rc, roff, rperm, rinv = oracle.permute_standard(ids, wl.E, align)
+    np.testing.assert_array_equal(counts.cpu().numpy(), rc)
+    np.testing.assert_array_equal(U.ws_view(ws, L.counts, wl.E).cpu().numpy(), rc)
+    np.testing.assert_array_equal(U.ws_view(ws, L.offsets, wl.E + 1).cpu().numpy(), roff)
+    np.testing.assert_array_equal(U.ws_view(ws, L.perm, L.perm_len).cpu().numpy(), rperm)
+    np.testing.assert_array_equal(U.ws_view(ws, L.inv, wl.M * wl.topk).cpu().numpy(), rinv)
+    assert U.ws_view(ws, L.status, 1).item() == 0
+
+
+BATCH_CASES = ["decode_fp8_m64", "decode_fp8_m256", "bf16_batched", "fp8_overflow"]
+
+
+def _batched_wl(name):
+    if name == "bf16_batched":
+        return WORKLOADS["dsv3_bf16"].replace(M=300, K=512, I=256, E=16, topk=4, format=FORMAT_BATCHED,
+                                               capacity=300, shared_I=0)
+    if name == "fp8_overflow":
+        return WORKLOADS["decode_fp8_m64"].replace(M=200, K=256, I=256, capacity=40)
+    return WORKLOADS[name]
+
+
+@pytest.mark.parametrize("name", BATCH_CASES)
+def test_prepare_batched_parity(name):
+    wl = _batched_wl(name)
+    ids, _ = _ids_from_oracle(wl)
+    d = make_inputs(wl.replace(E=1, I=128), seed=13, device="cpu")   # only x is used
+    x = d["x"]
+    p = U.problem(wl)
+    L = moe.workspace_layout(p)
+    ws = moe.empty_workspace(p)
+    fp8 = wl.act_quant == QUANT_FP8_G128
+    cap, E, K = wl.capacity, wl.E, wl.K
+    a_out = torch.full((E, cap, K), 0x7F if fp8 else 0, dtype=torch.uint8 if fp8 else U.torch_act_dtype(wl),
+                       device="cuda")
+    a_scale = torch.full((E, cap, K // 128), -1.0, device="cuda") if fp8 else None
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    moe.moe_prepare(p, x.cuda(), torch.from_numpy(ids).cuda(), a_out, a_scale, counts, ws)
+    torch.cuda.synchronize()
+    rc, rinv = oracle.permute_batched(ids, E, cap)
+    np.testing.assert_array_equal(counts.cpu().numpy(), rc)
+    np.testing.assert_array_equal(U.ws_view(ws, L.inv, wl.M * wl.topk).cpu().numpy(), rinv)
+    status = U.ws_view(ws, L.status, 1).item()
+    assert status == (moe.DEVICE_CAPACITY_OVERFLOW if (rc > cap).any() else 0)
+    a_cpu = a_out.cpu().reshape(E * cap, K)
+    flat = np.arange(wl.M * wl.topk)
+    kept = rinv >= 0
+    rows, toks = rinv[kept], flat[kept] // wl.topk
+    if fp8:
+        q, s = oracle.quant_g128(x.float().numpy())
+        np.testing.assert_array_equal(a_cpu.numpy()[rows], q[toks])
+        np.testing.assert_array_equal(a_scale.cpu().reshape(E * cap, K // 128).numpy()[rows], s[toks])
+    else:
+        np.testing.assert_array_equal(a_cpu.float().numpy()[rows], x.float().numpy()[toks])
+
+
+def test_prepare_flags_bad_ids():
+    wl = WORKLOADS["tiny_fp32"]
+    ids, _ = _ids_from_oracle(wl)
+    ids[3, 1] = wl.E          # out of range
+    ids[10, 0] = -5
+    p = U.problem(wl)
+    L = moe.workspace_layout(p)
+    ws = moe.empty_workspace(p)
+    counts = torch.empty(wl.E, dtype=torch.int32, device="cuda")
+    x = torch.zeros(wl.M, wl.K, device="cuda")
+    moe.moe_prepare(p, x, torch.from_numpy(ids).cuda(), None, None, counts, ws)
+    torch.cuda.synchronize()
+    assert U.ws_view(ws, L.status, 1).item() & moe.DEVICE_BAD_EXPERT_ID
+    inv = U.ws_view(ws, L.inv, wl.M * wl.topk).cpu().numpy()
+    assert inv[3 * wl.topk + 1] == -1 and inv[10 * wl.topk] == -1
+    good = (ids >= 0) & (ids < wl.E)
+    np.testing.assert_array_equal(counts.cpu().numpy(), np.bincount(ids[good], minlength=wl.E))
+
+
+# ---------------------------------------------------------------- experts
+
+SMALL = {
+    "tiny_fp32": WORKLOADS["tiny_fp32"],
+    "bf16_ragged": WORKLOADS["mixtral_bf16"].replace(M=300, K=384, I=192, E=7, topk=3, renormalize=False,
+                                                     logits_dist="normal"),
+    "bf16_batched": WORKLOADS["mixtral_bf16"].replace(M=150, K=256, I=128, E=5, topk=2, format=FORMAT_BATCHED,
+                                                      capacity=150, logits_dist="normal"),
+    "fp8_batched": WORKLOADS["decode_fp8_m64"].replace(M=90, K=384, I=256, E=5, topk=2, capacity=90),
+    "fp8_standard": WORKLOADS["decode_fp8_m64"].replace(M=90, K=256, I=256, E=6, topk=3,
+                                                        format=FORMAT_STANDARD, capacity=0),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_experts_parity_every_pair(name):
+    wl = SMALL[name]
+    d = make_inputs(wl, seed=14, device="cpu")
+    ids, _ = _ids_from_oracle(wl)
+    p = U.problem(wl)
+    ws = moe.empty_workspace(p)
+    g = U.to_cuda(d)
+    counts = torch.empty(wl.E, dtype=torch.int32, device="cuda")
+    fp8 = wl.act_quant == QUANT_FP8_G128
+    bat = U.batched(wl)
+    a_out = a_scale = None
+    if bat:
+        a_out = torch.empty(wl.E, wl.capacity, wl.K, dtype=torch.uint8 if fp8 else U.torch_act_dtype(wl),
+                            device="cuda")
+    elif fp8:
+        a_out = torch.empty(wl.M, wl.K, dtype=torch.uint8, device="cuda")
+    if fp8:
+        a_scale = torch.empty(a_out.shape[0] * (a_out.shape[1] if bat else 1), wl.K // 128, device="cuda")
+    moe.moe_prepare(p, g["x"], torch.from_numpy(ids).cuda(), a_out, a_scale, counts, ws)
+    rows = wl.E * wl.capacity if bat else wl.M * wl.topk
+    fused = torch.full((rows, wl.K), float("nan"), dtype=U.torch_act_dtype(wl), device="cuda")
+    moe.moe_experts(p, a_out if a_out is not None else g["x"], a_scale, g["w1"], g.get("w1_scale"), g["w2"],
+                    g.get("w2_scale"), counts, fused, ws)
+    torch.cuda.synchronize()
+    got = fused.float().cpu().numpy()
+    L = moe.workspace_layout(p)
+    inv = U.ws_view(ws, L.inv, wl.M * wl.topk).cpu().numpy()
+    ref = np.zeros((wl.M * wl.topk, wl.K))
+    mine = np.zeros_like(ref)
+    for m in range(wl.M):
+        a = oracle.input_row(d["x"], m, wl.act_dtype, wl.act_quant)
+        for j in range(wl.topk):
+            f = m * wl.topk + j
+            _, y = oracle.expert_row(a, int(ids[m, j]), d["w1"], d["w2"], wl.w_dtype, wl.I,
+                                     d.get("w1_scale"), d.get("w2_scale"), requant_fp8=fp8)
+            ref[f] = y
+            mine[f] = got[inv[f]] if bat else got[f]
+    assert np.all(np.isfinite(mine))
+    err = U.rel_err(mine, ref)
+    print(f"  {name}: max rel err {err:.3e}", flush=True)
+    assert err <= U.tol_for(wl)
+
+
+def test_finalize_parity():
+    for wl, bat in ((WORKLOADS["tiny_fp32"], False), (SMALL["bf16_ragged"], False), (SMALL["fp8_batched"], True)):
+        gen = torch.Generator().manual_seed(15)
+        p = U.problem(wl)
+        ws = moe.empty_workspace(p)
+        ids, w = _ids_from_oracle(wl)
+        rows = wl.E * wl.capacity if bat else wl.M * wl.topk
+        y = torch.randn(rows, wl.K, generator=gen).to(U.torch_act_dtype(wl))
+        if bat:   # the combine reads the pair -> row map that prepare leaves in the workspace
+            counts = torch.empty(wl.E, dtype=torch.int32, device="cuda")
+            a_out = torch.empty(wl.E, wl.capacity, wl.K, dtype=torch.uint8, device="cuda")
+            a_s = torch.empty(wl.E * wl.capacity, wl.K // 128, device="cuda")
+            x = torch.zeros(wl.M, wl.K, dtype=U.torch_act_dtype(wl), device="cuda")
+            moe.moe_prepare(p, x, torch.from_numpy(ids).cuda(), a_out, a_s, counts, ws)
+            _, inv = oracle.permute_batched(ids, wl.E, wl.capacity)
+            ypairs = y.float().numpy()[np.maximum(inv, 0)]
+            keep = (inv >= 0).astype(np.int32)
+        else:
+            ypairs, keep = y.float().numpy(), None
+        out = torch.empty(wl.M, wl.K, dtype=U.torch_act_dtype(wl), device="cuda")
+        wt = torch.from_numpy(w.astype(np.float32))
+        moe.moe_finalize(p, y.cuda(), wt.cuda(), out, ws)
+        torch.cuda.synchronize()
+        ref = oracle.combine(wt.double().numpy(), ypairs.reshape(wl.M, wl.topk, wl.K), keep)
+        assert U.rel_err(out.float().cpu().numpy(), ref) <= U.tol_for(wl)
+
+
+# ---------------------------------------------------------------- whole layer
+
+FULL = list(WORKLOADS)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_forward_parity_full_size(name):
+    wl = WORKLOADS[name]
+    small = wl.M * wl.K * wl.I * wl.E < 2 ** 28
+    d = make_inputs(wl, seed=0, device="cpu" if small else "cuda")
+    g = U.to_cuda(d)
+    out, sout, ws, p = U.run_forward(wl, g)
+    torch.cuda.synchronize()
+    L = moe.workspace_layout(p)
+    # every routing / counting / permutation entry
+    rids, rw = oracle.route(d["logits"], wl.topk, wl.scoring, wl.renormalize)
+    np.testing.assert_array_equal(U.ws_view(ws, L.topk_ids, wl.M * wl.topk).cpu().numpy().reshape(wl.M, -1), rids)
+    tw = U.ws_view(ws, L.topk_weights, wl.M * wl.topk, torch.float32).cpu().numpy().reshape(wl.M, -1)
+    np.testing.assert_allclose(tw, rw, rtol=U.WEIGHT_RTOL, atol=1e-7)
+    if U.batched(wl):
+        rc, rinv = oracle.permute_batched(rids, wl.E, wl.capacity)
+        np.testing.assert_array_equal(U.ws_view(ws, L.inv, wl.M * wl.topk).cpu().numpy(), rinv)
+    else:
+        rc, roff, rperm, rinv = oracle.permute_standard(rids, wl.E, 1)
+        np.testing.assert_array_equal(U.ws_view(ws, L.perm, L.perm_len).cpu().numpy(), rperm)
+        np.testing.assert_array_equal(U.ws_view(ws, L.offsets, wl.E + 1).cpu().numpy(), roff)
+    np.testing.assert_array_equal(U.ws_view(ws, L.counts, wl.E).cpu().numpy(), rc)
+    assert U.ws_view(ws, L.status, 1).item() == 0
+    # output rows: all of them for small problems, a seeded sample otherwise
+    toks = list(range(wl.M)) if small else sample_tokens(wl.M, 10, seed=1)
+    ref, _, _ = oracle.moe_tokens(wl, d, toks)
+    got = out.float().cpu().numpy()[toks]
+    assert np.all(np.isfinite(got))
+    err = U.rel_err(got, ref)
+    print(f"  {name}: {len(toks)} rows, max rel err {err:.3e}", flush=True)
+    assert err <= U.tol_for(wl)
+    if wl.shared_I:
+        sref = oracle.dense_mlp_tokens(d["x"], d["w1s"], d["w2s"], wl.shared_I, wl.act_dtype, toks)
+        serr = U.rel_err(sout.float().cpu().numpy()[toks], sref)
+        print(f"  {name}: shared expert max rel err {serr:.3e}", flush=True)
+        assert serr <= U.tol_for(wl)
+
+
+# ---------------------------------------------------------------- edge cases
+
+EDGE = {
+    "M1": WORKLOADS["mixtral_bf16"].replace(M=1, K=256, I=128, E=8, topk=2),
+    "k_eq_E": WORKLOADS["mixtral_bf16"].replace(M=37, K=256, I=128, E=4, topk=4, logits_dist="normal"),
+    "E1_k1": WORKLOADS["tiny_fp32"].replace(M=130, E=1, topk=1),
+    "fp8_M1": WORKLOADS["decode_fp8_m64"].replace(M=1, K=256, I=128, E=8, capacity=8),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_forward_edge_shapes(name):
+    wl = EDGE[name]
+    d = make_inputs(wl, seed=16, device="cpu")
+    out, _, ws, _ = U.run_forward(wl, U.to_cuda(d))
+    torch.cuda.synchronize()
+    ref, _, _ = oracle.moe_tokens(wl, d)
+    assert U.rel_err(out.float().cpu().numpy(), ref) <= U.tol_for(wl)
+
+
+def test_forward_empty_batch_is_noop():
+    wl = WORKLOADS["tiny_fp32"].replace(M=0)
+    p = U.problem(wl)
+    out = torch.empty(0, wl.K, device="cuda")
+    d = make_inputs(wl.replace(M=1), seed=0, device="cuda")
+    moe.moe_forward(p, d["logits"][:0], d["x"][:0], d["w1"], None, d["w2"], None, out,
+                    torch.empty(16, dtype=torch.uint8, device="cuda"))
+
+
+def test_zero_count_expert_nan_weights_change_nothing():
+    wl = SMALL["bf16_ragged"]
+    d = make_inputs(wl, seed=17, device="cpu")
+    d["logits"][:, 2] = -1e4                      # expert 2 never routed
+    g = U.to_cuda(d)
+    base, _, _, _ = U.run_forward(wl, g)
+    g["w1"][2] = float("nan")
+    g["w2"][2] = float("nan")
+    poisoned, _, ws, p = U.run_forward(wl, g)
+    torch.cuda.synchronize()
+    assert U.ws_view(ws, moe.workspace_layout(p).counts, wl.E)[2].item() == 0
+    assert torch.isfinite(poisoned.float()).all()
+    assert torch.equal(base, poisoned)
+
+
+def test_maximal_skew_all_tokens_same_experts():
+    wl = SMALL["bf16_ragged"].replace(M=700)
+    d = make_inputs(wl, seed=18, device="cpu")
+    d["logits"][:, :wl.topk] += 100.0             # every token picks experts 0..k-1
+    out, _, ws, p = U.run_forward(wl, U.to_cuda(d))
+    torch.cuda.synchronize()
+    counts = U.ws_view(ws, moe.workspace_layout(p).counts, wl.E).cpu().numpy()
+    assert counts[:wl.topk].tolist() == [wl.M] * wl.topk and counts[wl.topk:].sum() == 0
+    toks = sample_tokens(wl.M, 40, seed=2)
+    ref, _, _ = oracle.moe_tokens(wl, d, toks)
+    assert U.rel_err(out.float().cpu().numpy()[toks], ref) <= U.tol_for(wl)
+
+
+def test_batched_capacity_overflow_drops_and_flags():
+    wl = SMALL["fp8_batched"].replace(M=120, capacity=20)
+    d = make_inputs(wl, seed=19, device="cpu")
+    out, _, ws, p = U.run_forward(wl, U.to_cuda(d))
+    torch.cuda.synchronize()
+    assert U.ws_view(ws, moe.workspace_layout(p).status, 1).item() == moe.DEVICE_CAPACITY_OVERFLOW
+    ref, _, _ = oracle.moe_tokens(wl, d)        # the oracle drops the same pairs
+    assert U.rel_err(out.float().cpu().numpy(), ref) <= U.tol_for(wl)
+
+
+def test_standard_and_batched_agree_bitwise():
+    wl = SMALL["bf16_ragged"]
+    d = U.to_cuda(make_inputs(wl, seed=20, device="cpu"))
+    a, _, _, _ = U.run_forward(wl, d)
+    b, _, _, _ = U.run_forward(wl.replace(format=FORMAT_BATCHED, capacity=wl.M), d)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_forward_is_deterministic():
+    wl = WORKLOADS["dsv3_bf16"].replace(M=512, E=64, I=256, K=512, shared_I=256)
+    d = U.to_cuda(make_inputs(wl, seed=21, device="cpu"))
+    a, sa, _, _ = U.run_forward(wl, d)
+    b, sb, _, _ = U.run_forward(wl, d)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(sa, sb)
+
+
+def test_stage_calls_equal_forward():
+    """route -> prepare -> experts -> finalize through the separate calls
+    gives exactly what moe_forward gives (same kernels, same order)."""
+    for wl in (SMALL["bf16_ragged"], SMALL["fp8_batched"]):
+        d = U.to_cuda(make_inputs(wl, seed=22, device="cpu"))
+        ref, _, _, p = U.run_forward(wl, d)
+        ws = moe.empty_workspace(p)
+        w = torch.empty(wl.M, wl.topk, device="cuda")
+        ids = torch.empty(wl.M, wl.topk, dtype=torch.int32, device="cuda")
+        moe.moe_route(p, d["logits"], w, ids)
+        counts = torch.empty(wl.E, dtype=torch.int32, device="cuda")
+        fp8 = wl.act_quant == QUANT_FP8_G128
+        bat = U.batched(wl)
+        a_out = a_s = None
+        if bat:
+            a_out = torch.empty(wl.E, wl.capacity, wl.K, dtype=torch.uint8 if fp8 else torch.bfloat16, device="cuda")
+            if fp8:
+                a_s = torch.empty(wl.E * wl.capacity, wl.K // 128, device="cuda")
+        moe.moe_prepare(p, d["x"], ids, a_out, a_s, counts, ws)
+        rows = wl.E * wl.capacity if bat else wl.M * wl.topk
+        fused = torch.empty(rows, wl.K, dtype=torch.bfloat16, device="cuda")
+        moe.moe_experts(p, a_out if bat else d["x"], a_s, d["w1"], d.get("w1_scale"), d["w2"], d.get("w2_scale"),
+                        counts, fused, ws)
+        out = torch.empty_like(ref)
+        moe.moe_finalize(p, fused, w, out, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+
+
+def test_graph_replay_matches_eager():
+    """Capture the whole layer (with the shared expert on its aux stream) in one
+    graph; replay it with fresh inputs copied into the captured buffers and
+    compare every replay with an eager run on the same inputs."""
+    wl = WORKLOADS["dsv3_bf16"].replace(M=256, E=32, I=256, K=512, shared_I=256)
+    d = U.to_cuda(make_inputs(wl, seed=23, device="cpu"))
+    p = U.problem(wl)
+    ws = moe.empty_workspace(p)
+    out = torch.empty(wl.M, wl.K, dtype=torch.bfloat16, device="cuda")
+    sout = torch.empty_like(out)
+    streams = moe.SharedExpertStreams()
+    U.run_forward(wl, d, ws=ws, p=p, out=out, shared_out=sout, streams=streams)   # warm-up
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            moe.moe_forward(p, d["logits"], d["x"], d["w1"], None, d["w2"], None, out, ws,
+                            shared=(d["w1s"], d["w2s"], sout), shared_streams=streams)
+    torch.cuda.synchronize()
+    ews = moe.empty_workspace(p)
+    for it in range(5):
+        fresh = make_inputs(wl, seed=100 + it, device="cpu")
+        d["logits"].copy_(fresh["logits"].cuda())
+        d["x"].copy_(fresh["x"].cuda())
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        e_out, e_sout, _, _ = U.run_forward(wl, d, ws=ews, p=p)
+        torch.cuda.synchronize()
+        assert torch.equal(out, e_out), it
+        assert torch.equal(sout, e_sout), it
