@@ -155,7 +155,12 @@ moe_status do_experts(const moe_problem &p, const void *a, const float *a_scale,
   int32_t *tiles = at<int32_t>(ws, L.tiles);
   int32_t *status = at<int32_t>(ws, L.status);
   int32_t *perm = standard ? at<int32_t>(ws, L.perm) : nullptr;
-  MOE_HIP(launch_plan_tiles(p, counts, at<int32_t>(ws, L.offsets), L.perm_len, (int)L.tile_rows,
+  // Weight streaming while the average expert holds no more rows than one
+  // streaming tile (weights then dominate the bytes); MFMA tiles otherwise.
+  const bool streaming = p.w_dtype != MOE_DTYPE_F32 && I % 128 == 0 &&
+                         p.M * p.topk <= p.E * (int64_t)stream_gemm_tile_rows(p.w_dtype);
+  const int tile_rows = streaming ? stream_gemm_tile_rows(p.w_dtype) : (int)L.tile_rows;
+  MOE_HIP(launch_plan_tiles(p, counts, at<int32_t>(ws, L.offsets), L.perm_len, tile_rows,
                             (int)L.max_tiles, tiles, status, s));
   record(ev, 2, s);
   GemmTiles gt;
@@ -179,8 +184,12 @@ moe_status do_experts(const moe_problem &p, const void *a, const float *a_scale,
   g1.ldo = I;
   g1.half_n = I;
   g1.t = gt;
-  MOE_HIP(launch_grouped_gemm(p.w_dtype, fp8 ? MOE_DTYPE_F32 : p.act_dtype, kGemmGatedAct, g1,
-                              (int)(I / 64), s));
+  if (streaming)
+    MOE_HIP(launch_stream_gemm(p.w_dtype, fp8 ? MOE_DTYPE_F32 : p.act_dtype, kGemmGatedAct, g1,
+                               (int)(I / 128), s));
+  else
+    MOE_HIP(launch_grouped_gemm(p.w_dtype, fp8 ? MOE_DTYPE_F32 : p.act_dtype, kGemmGatedAct, g1,
+                                (int)(I / 64), s));
   record(ev, 3, s);
   if (fp8)
     MOE_HIP(launch_quant_rows(at<float>(ws, L.act), tiles, (int)L.max_tiles, I, at<uint8_t>(ws, L.act_q),
@@ -202,7 +211,10 @@ moe_status do_experts(const moe_problem &p, const void *a, const float *a_scale,
   g2.out_perm = perm;
   g2.half_n = 0;
   g2.t = gt;
-  MOE_HIP(launch_grouped_gemm(p.w_dtype, p.act_dtype, kGemmDown, g2, (int)(p.K / 128), s));
+  if (streaming)
+    MOE_HIP(launch_stream_gemm(p.w_dtype, p.act_dtype, kGemmDown, g2, (int)(p.K / 128), s));
+  else
+    MOE_HIP(launch_grouped_gemm(p.w_dtype, p.act_dtype, kGemmDown, g2, (int)(p.K / 128), s));
   record(ev, 4, s);
   return MOE_OK;
 }

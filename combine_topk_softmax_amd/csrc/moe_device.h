@@ -136,6 +136,11 @@ hipError_t launch_quant_rows(const float *in, const int32_t *tiles, int max_tile
                              uint8_t *q, float *scale, hipStream_t s);
 hipError_t launch_grouped_gemm(int w_dtype, int out_dtype, GemmKind kind, const GemmParams &g,
                                int n_tiles, hipStream_t s);
+// Weight-streaming variant (HBM-bound regime): gated tiles cover 128 gate
+// columns, down tiles 128 output columns; rows per tile below.
+int stream_gemm_tile_rows(int w_dtype);
+hipError_t launch_stream_gemm(int w_dtype, int out_dtype, GemmKind kind, const GemmParams &g, int n_tiles,
+                              hipStream_t s);
 hipError_t launch_combine(const moe_problem &p, const void *fused_out, const float *topk_w,
                           const int32_t *inv, void *out, hipStream_t s);
 

@@ -1,0 +1,305 @@
+// Weight-streaming grouped GEMM for the HBM-bound regime (a few hundred rows
+// per expert at most): decode-sized batches and prefill whose per-expert row
+// count is below the MFMA/HBM ridge.  Same computation as grouped_gemm.hip --
+// the gated GEMM act = silu(A w1_gate) * (A w1_up) or the down GEMM
+// out = act w2^T with the unpermute in its epilogue (modular_kernel.py page:
+// FusedMoEPermuteExpertsUnpermute, "matmul + act_mul + optionally quant +
+// matmul"; the worst-tokens page: the grouped GEMM is masked by per-expert
+// counts read on the device) -- organised around reading every weight byte
+// exactly once:
+//
+//  * one workgroup = one expert's rows (up to kTmax, masked by the device
+//    count in 16-row MFMA blocks) x a panel of weight rows, so an expert's
+//    weights are streamed once whatever its row count;
+//  * each of the 8 wavefronts owns its own 16-row weight blocks, which no
+//    other wavefront needs: they go straight from HBM into MFMA B fragments in
+//    registers, prefetched D K-steps ahead (no LDS round trip);
+//  * the activation rows, shared by all wavefronts, are staged through a
+//    double-buffered LDS tile (XOR-swizzled 16-byte chunks) two K-steps ahead;
+//  * work items are dealt out XCD by XCD: consecutive items of one expert land
+//    on the same XCD, so its activation rows stay in that XCD's L2.
+//
+// MFMA: v_mfma_f32_16x16x32_bf16 or _fp8_fp8 (OCP e4m3; fp32 block scales
+// applied per 128-wide K block).  Inside each 128-byte K-step a lane of group
+// q = lane/16 holds 32 contiguous bytes; MFMA step t takes bytes
+// [t*F, t*F + F) of them (F = 16 for bf16, 8 for fp8).  A and B use the same
+// mapping, so the k permutation this implies cancels in the dot product.
+#include "moe_device.h"
+
+namespace moe {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int EB>
+struct Mfma16;
+
+template <>
+struct Mfma16<2> {
+  static constexpr int kSteps = 2;  // 16x16x32 steps per 128-byte K-step
+  typedef bf16x8 frag;
+  __device__ static f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Mfma16<1> {
+  static constexpr int kSteps = 4;
+  typedef long frag;
+  __device__ static f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
+  }
+};
+
+__device__ __forceinline__ int swz(int row, int b) {
+  return row * 128 + ((((b >> 4) ^ (row & 7)) << 4) | (b & 15));
+}
+
+template <typename F>
+__device__ __forceinline__ F frag_at(const uint4 (&v)[2], int t) {
+  if constexpr (sizeof(F) == 16) {
+    return __builtin_bit_cast(F, v[t]);
+  } else {
+    const uint4 q = v[t >> 1];
+    const uint2 h = (t & 1) ? make_uint2(q.z, q.w) : make_uint2(q.x, q.y);
+    return __builtin_bit_cast(F, h);
+  }
+}
+
+constexpr int kThreads = 512;
+
+template <int EB, bool GATED, bool OUT_BF16, int NBW, int D, int TMAX>
+__global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams g, int n_tiles) {
+  using MM = Mfma16<EB>;
+  using frag = typename MM::frag;
+  constexpr bool kScaled = EB == 1;
+  constexpr int kMB = TMAX / 16;            // MFMA row blocks
+  constexpr int kARows = TMAX / 64;         // A rows per thread per K-step
+  constexpr int kFrag = 32 / MM::kSteps;    // bytes per lane per MFMA step
+  constexpr int U = D == 1 ? 2 : (D % 2 == 0 ? D : 2 * D);   // unroll = lcm(2, D)
+  static_assert(!GATED || NBW == 2, "a gated wave holds one gate and one up block");
+
+  __shared__ __attribute__((aligned(16))) uint8_t As[2][TMAX * 128];
+  __shared__ float Sa[2][TMAX];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int total = *g.t.tile_count * n_tiles;
+  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+  const int per = (total + 7) >> 3;
+  const int item = xcd * per + local;
+  if (local >= per || item >= total) return;
+  const int c = item / n_tiles, nt = item - c * n_tiles;
+  const int32_t *tile = g.t.tiles + (int64_t)c * 4;
+  const int e = tile[0];
+  const int64_t row0 = (int64_t)tile[1] + tile[2];
+  const int T = tile[3];
+  const int nmb = (T + 15) >> 4;
+  const int64_t row_bytes = g.Kred * EB;
+  const int nk = (int)(row_bytes / 128);
+  const int q = lane >> 4, r16 = lane & 15;
+
+  // ---- weight rows of this wavefront (NBW blocks of 16 rows)
+  const uint8_t *wsrc[NBW];
+  const float *wscale[NBW];
+  const int64_t kblocks = g.Kred / 128;
+#pragma unroll
+  for (int b = 0; b < NBW; ++b) {
+    int64_t wrow0;
+    if (GATED)
+      wrow0 = (b ? g.half_n : 0) + (int64_t)nt * 128 + wv * 16;
+    else
+      wrow0 = (int64_t)nt * (128 * NBW) + wv * (16 * NBW) + b * 16;
+    wsrc[b] = reinterpret_cast<const uint8_t *>(g.w) + ((int64_t)e * g.Nw + wrow0 + r16) * row_bytes + q * 32;
+    wscale[b] = kScaled ? g.w_scale + ((int64_t)e * (g.Nw / 128) + wrow0 / 128) * kblocks : nullptr;
+  }
+
+  // ---- activation rows this thread stages (row index in A, or -1)
+  const int ach = tid & 7;
+  int64_t arow[kARows];
+#pragma unroll
+  for (int i = 0; i < kARows; ++i) {
+    const int r = (tid >> 3) + 64 * i;
+    arow[i] = -2;                            // -2: not needed (beyond the last row block)
+    if (r < nmb * 16) {
+      arow[i] = -1;                          // -1: zero row (past the count)
+      if (r < T) {
+        const int64_t s = row0 + r;
+        int64_t a = s;
+        if (g.perm) {
+          const int f = g.perm[s];
+          a = (f >= 0 && f < g.n_pairs) ? f / g.topk : -1;
+        }
+        arow[i] = a;
+      }
+    }
+  }
+  int64_t srow = -1;                          // fp8: this thread's row scale source (tid < T)
+  if (kScaled && tid < T) {
+    const int64_t s = row0 + tid;
+    srow = s;
+    if (g.perm) {
+      const int f = g.perm[s];
+      srow = (f >= 0 && f < g.n_pairs) ? f / g.topk : -1;
+    }
+  }
+  const uint8_t *abase = reinterpret_cast<const uint8_t *>(g.a) + ach * 16;
+
+  uint4 ra[2][kARows];
+  float rsa[2] = {0.0f, 0.0f};
+  auto loadA = [&](int j, int ks) {
+#pragma unroll
+    for (int i = 0; i < kARows; ++i) {
+      if (arow[i] >= 0)
+        ra[j][i] = *reinterpret_cast<const uint4 *>(abase + arow[i] * row_bytes + (int64_t)ks * 128);
+      else
+        ra[j][i] = make_uint4(0, 0, 0, 0);
+    }
+    if constexpr (kScaled) rsa[j] = srow >= 0 ? g.a_scale[srow * kblocks + ks] : 0.0f;
+  };
+  auto storeA = [&](int j, int st) {
+#pragma unroll
+    for (int i = 0; i < kARows; ++i) {
+      if (arow[i] != -2) {
+        const int r = (tid >> 3) + 64 * i;
+        *reinterpret_cast<uint4 *>(&As[st][swz(r, ach * 16)]) = ra[j][i];
+      }
+    }
+    if constexpr (kScaled)
+      if (tid < TMAX) Sa[st][tid] = rsa[j];
+  };
+
+  uint4 wb[D][NBW][2];
+  float wsv[D][NBW];
+  auto loadW = [&](int j, int ks) {
+#pragma unroll
+    for (int b = 0; b < NBW; ++b) {
+      const uint4 *p = reinterpret_cast<const uint4 *>(wsrc[b] + (int64_t)ks * 128);
+      wb[j][b][0] = p[0];
+      wb[j][b][1] = p[1];
+      if constexpr (kScaled) wsv[j][b] = wscale[b][ks];
+    }
+  };
+
+  f32x4 acc[kMB][NBW];
+#pragma unroll
+  for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+    for (int b = 0; b < NBW; ++b) acc[mb][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto compute = [&](int st, int j) {
+    const uint8_t *A = As[st];
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb) {
+      if (mb < nmb) {  // uniform
+      const int ar = mb * 16 + r16;
+      f32x4 part[NBW];
+      if constexpr (kScaled)
+#pragma unroll
+        for (int b = 0; b < NBW; ++b) part[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int t = 0; t < MM::kSteps; ++t) {
+        const frag af = *reinterpret_cast<const frag *>(A + swz(ar, q * 32 + t * kFrag));
+#pragma unroll
+        for (int b = 0; b < NBW; ++b) {
+          const frag bf = frag_at<frag>(wb[j][b], t);
+          if constexpr (kScaled)
+            part[b] = MM::mma(af, bf, part[b]);
+          else
+            acc[mb][b] = MM::mma(af, bf, acc[mb][b]);
+        }
+      }
+      if constexpr (kScaled) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float sa = Sa[st][mb * 16 + q * 4 + i];
+#pragma unroll
+          for (int b = 0; b < NBW; ++b) acc[mb][b][i] += part[b][i] * (sa * wsv[j][b]);
+        }
+      }
+      }
+    }
+  };
+
+  // ---- pipeline: A two K-steps ahead (registers -> LDS), weights D ahead.
+  loadA(0, 0);
+  if (nk > 1) loadA(1, 1);
+#pragma unroll
+  for (int j = 0; j < D; ++j)
+    if (j < nk) loadW(j, j);
+  storeA(0, 0);
+  __syncthreads();
+
+  for (int kb = 0; kb < nk; kb += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = kb + u;
+      if (k < nk) {
+        if (k + 2 < nk) loadA(u & 1, k + 2);
+        compute(u & 1, u % D);
+        if (k + D < nk) loadW(u % D, k + D);
+        if (k + 1 < nk) storeA((u + 1) & 1, (u + 1) & 1);
+        __syncthreads();
+      }
+    }
+  }
+
+  // ---- epilogue: 16x16 block, lane holds column r16, rows 4*q + i.
+#pragma unroll
+  for (int mb = 0; mb < kMB; ++mb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = mb * 16 + q * 4 + i;
+      if (r >= T) continue;
+      const int64_t slot = row0 + r;
+      if constexpr (GATED) {
+        const float gt = acc[mb][0][i], up = acc[mb][1][i];
+        const float v = gt / (1.0f + expf(-gt)) * up;
+        const int64_t col = (int64_t)nt * 128 + wv * 16 + r16;
+        if constexpr (OUT_BF16)
+          reinterpret_cast<uint16_t *>(g.out)[slot * g.ldo + col] = f32_to_bf16_bits(v);
+        else
+          reinterpret_cast<float *>(g.out)[slot * g.ldo + col] = v;
+      } else {
+        const int64_t orow = g.out_perm ? g.out_perm[slot] : slot;
+        if (orow < 0 || (g.out_perm && orow >= g.n_pairs)) continue;
+#pragma unroll
+        for (int b = 0; b < NBW; ++b) {
+          const int64_t col = (int64_t)nt * (128 * NBW) + wv * (16 * NBW) + b * 16 + r16;
+          if constexpr (OUT_BF16)
+            reinterpret_cast<uint16_t *>(g.out)[orow * g.ldo + col] = f32_to_bf16_bits(acc[mb][b][i]);
+          else
+            reinterpret_cast<float *>(g.out)[orow * g.ldo + col] = acc[mb][b][i];
+        }
+      }
+    }
+  }
+}
+
+template <int EB, bool GATED, int NBW, int D, int TMAX>
+hipError_t launch_cfg(int out_dtype, const GemmParams &g, int n_tiles, hipStream_t s) {
+  const int64_t items = (int64_t)g.t.max_tiles * n_tiles;
+  dim3 grid((unsigned)(((items + 7) / 8) * 8)), block(kThreads);
+  if (out_dtype == MOE_DTYPE_BF16)
+    stream_gemm_kernel<EB, GATED, true, NBW, D, TMAX><<<grid, block, 0, s>>>(g, n_tiles);
+  else
+    stream_gemm_kernel<EB, GATED, false, NBW, D, TMAX><<<grid, block, 0, s>>>(g, n_tiles);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int stream_gemm_tile_rows(int w_dtype) { return w_dtype == MOE_DTYPE_FP8_E4M3 ? 128 : 256; }
+
+hipError_t launch_stream_gemm(int w_dtype, int out_dtype, GemmKind kind, const GemmParams &g, int n_tiles,
+                              hipStream_t s) {
+  const bool fp8 = w_dtype == MOE_DTYPE_FP8_E4M3;
+  if (kind == kGemmGatedAct)
+    return fp8 ? launch_cfg<1, true, 2, 2, 128>(out_dtype, g, n_tiles, s)
+               : launch_cfg<2, true, 2, 2, 256>(out_dtype, g, n_tiles, s);
+  return fp8 ? launch_cfg<1, false, 1, 4, 128>(out_dtype, g, n_tiles, s)
+             : launch_cfg<2, false, 1, 4, 256>(out_dtype, g, n_tiles, s);
+}
+
+}  // namespace moe
