@@ -110,11 +110,15 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmParams g) {
 
   // Source rows of this thread's 4 A chunks and 4 B chunks per K-step.
   const uint8_t *a_src[4];
+  bool a_ok[4];
   const uint8_t *b_src[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = (tid >> 3) + 32 * i;
-    a_src[i] = nullptr;
+    // rows past the count read row 0 (no branch around the load) and are
+    // zeroed on their way into LDS
+    a_src[i] = reinterpret_cast<const uint8_t *>(g.a) + chunk * 16;
+    a_ok[i] = false;
     if (r < nrows) {
       const int64_t s = row0 + r;
       int64_t arow = s;
@@ -122,7 +126,10 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmParams g) {
         const int f = g.perm[s];
         arow = (f >= 0 && f < g.n_pairs) ? f / g.topk : -1;
       }
-      if (arow >= 0) a_src[i] = reinterpret_cast<const uint8_t *>(g.a) + arow * row_bytes + chunk * 16;
+      if (arow >= 0) {
+        a_src[i] = reinterpret_cast<const uint8_t *>(g.a) + arow * row_bytes + chunk * 16;
+        a_ok[i] = true;
+      }
     }
     int64_t wrow;
     if (GATED)
@@ -132,7 +139,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmParams g) {
     b_src[i] = reinterpret_cast<const uint8_t *>(g.w) + ((int64_t)e * g.Nw + wrow) * row_bytes + chunk * 16;
   }
   // fp8: per-row activation scale (thread tid < 128 owns row tid), per-block weight scales.
-  const float *sa_src = nullptr;
+  const float *sa_src = g.a_scale;
+  bool sa_ok = false;
   const float *sw_src[2] = {nullptr, nullptr};
   const int64_t kblocks = g.Kred / 128;
   if constexpr (kScaled) {
@@ -143,7 +151,10 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmParams g) {
         const int f = g.perm[s];
         arow = (f >= 0 && f < g.n_pairs) ? f / g.topk : -1;
       }
-      if (arow >= 0) sa_src = g.a_scale + arow * kblocks;
+      if (arow >= 0) {
+        sa_src = g.a_scale + arow * kblocks;
+        sa_ok = true;
+      }
     }
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
@@ -174,20 +185,20 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmParams g) {
     const int64_t off = (int64_t)ks * kRowBytes;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ra[i] = a_src[i] ? *reinterpret_cast<const uint4 *>(a_src[i] + off) : make_uint4(0, 0, 0, 0);
+      ra[i] = *reinterpret_cast<const uint4 *>(a_src[i] + off);
       rb[i] = *reinterpret_cast<const uint4 *>(b_src[i] + off);
     }
-    if constexpr (kScaled) sa_reg = sa_src ? sa_src[ks] : 0.0f;
+    if constexpr (kScaled) sa_reg = sa_src[ks];
   };
   auto lstore = [&](int st) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = (tid >> 3) + 32 * i;
-      *reinterpret_cast<uint4 *>(&lds[st][0][swz(r, chunk * 16)]) = ra[i];
+      *reinterpret_cast<uint4 *>(&lds[st][0][swz(r, chunk * 16)]) = a_ok[i] ? ra[i] : make_uint4(0, 0, 0, 0);
       *reinterpret_cast<uint4 *>(&lds[st][1][swz(r, chunk * 16)]) = rb[i];
     }
     if constexpr (kScaled)
-      if (tid < 128) lds_sa[st][tid] = sa_reg;
+      if (tid < 128) lds_sa[st][tid] = sa_ok ? sa_reg : 0.0f;
   };
   auto compute = [&](int st, int ks) {
     const uint8_t *As = lds[st][0];
@@ -242,11 +253,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmParams g) {
   gload(0);
   lstore(0);
   __syncthreads();
+  // The last step reloads itself instead of branching around the loads.
   for (int ks = 0; ks < nk; ++ks) {
     const int st = ks & 1;
-    if (ks + 1 < nk) gload(ks + 1);
+    gload(min(ks + 1, nk - 1));
     compute(st, ks);
-    if (ks + 1 < nk) lstore(st ^ 1);
+    lstore(st ^ 1);
     __syncthreads();
   }
 

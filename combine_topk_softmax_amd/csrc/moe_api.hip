@@ -157,7 +157,7 @@ moe_status do_experts(const moe_problem &p, const void *a, const float *a_scale,
   int32_t *perm = standard ? at<int32_t>(ws, L.perm) : nullptr;
   // Weight streaming while the average expert holds no more rows than one
   // streaming tile (weights then dominate the bytes); MFMA tiles otherwise.
-  const bool streaming = p.w_dtype != MOE_DTYPE_F32 && I % 128 == 0 &&
+  const bool streaming = p.w_dtype != MOE_DTYPE_F32 && stream_gemm_fits(p.w_dtype, p.K, I) &&
                          p.M * p.topk <= p.E * (int64_t)stream_gemm_tile_rows(p.w_dtype);
   const int tile_rows = streaming ? stream_gemm_tile_rows(p.w_dtype) : (int)L.tile_rows;
   MOE_HIP(launch_plan_tiles(p, counts, at<int32_t>(ws, L.offsets), L.perm_len, tile_rows,

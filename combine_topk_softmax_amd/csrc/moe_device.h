@@ -139,6 +139,7 @@ hipError_t launch_grouped_gemm(int w_dtype, int out_dtype, GemmKind kind, const 
 // Weight-streaming variant (HBM-bound regime): gated tiles cover 128 gate
 // columns, down tiles 128 output columns; rows per tile below.
 int stream_gemm_tile_rows(int w_dtype);
+bool stream_gemm_fits(int w_dtype, int64_t K, int64_t I);
 hipError_t launch_stream_gemm(int w_dtype, int out_dtype, GemmKind kind, const GemmParams &g, int n_tiles,
                               hipStream_t s);
 hipError_t launch_combine(const moe_problem &p, const void *fused_out, const float *topk_w,

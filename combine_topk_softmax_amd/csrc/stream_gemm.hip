@@ -146,28 +146,27 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
   }
   const uint8_t *abase = reinterpret_cast<const uint8_t *>(g.a) + ach * 16;
 
+  // Loads are unconditional (rows past the count read row 0, K-steps past the
+  // end re-read the last one) so that the loop body has no branches around
+  // memory operations; the zero mask is applied when the rows reach LDS.
   uint4 ra[2][kARows];
   float rsa[2] = {0.0f, 0.0f};
   auto loadA = [&](int j, int ks) {
 #pragma unroll
-    for (int i = 0; i < kARows; ++i) {
-      if (arow[i] >= 0)
-        ra[j][i] = *reinterpret_cast<const uint4 *>(abase + arow[i] * row_bytes + (int64_t)ks * 128);
-      else
-        ra[j][i] = make_uint4(0, 0, 0, 0);
-    }
-    if constexpr (kScaled) rsa[j] = srow >= 0 ? g.a_scale[srow * kblocks + ks] : 0.0f;
+    for (int i = 0; i < kARows; ++i)
+      ra[j][i] = *reinterpret_cast<const uint4 *>(abase + (arow[i] >= 0 ? arow[i] : 0) * row_bytes +
+                                                   (int64_t)ks * 128);
+    if constexpr (kScaled) rsa[j] = g.a_scale[(srow >= 0 ? srow : 0) * kblocks + ks];
   };
   auto storeA = [&](int j, int st) {
 #pragma unroll
     for (int i = 0; i < kARows; ++i) {
-      if (arow[i] != -2) {
-        const int r = (tid >> 3) + 64 * i;
-        *reinterpret_cast<uint4 *>(&As[st][swz(r, ach * 16)]) = ra[j][i];
-      }
+      const int r = (tid >> 3) + 64 * i;
+      const uint4 v = arow[i] >= 0 ? ra[j][i] : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4 *>(&As[st][swz(r, ach * 16)]) = v;
     }
     if constexpr (kScaled)
-      if (tid < TMAX) Sa[st][tid] = rsa[j];
+      if (tid < TMAX) Sa[st][tid] = srow >= 0 ? rsa[j] : 0.0f;
   };
 
   uint4 wb[D][NBW][2];
@@ -223,11 +222,11 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
   };
 
   // ---- pipeline: A two K-steps ahead (registers -> LDS), weights D ahead.
+  // The host guarantees nk % U == 0.
   loadA(0, 0);
-  if (nk > 1) loadA(1, 1);
+  loadA(1, min(1, nk - 1));
 #pragma unroll
-  for (int j = 0; j < D; ++j)
-    if (j < nk) loadW(j, j);
+  for (int j = 0; j < D; ++j) loadW(j, min(j, nk - 1));
   storeA(0, 0);
   __syncthreads();
 
@@ -235,13 +234,11 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int k = kb + u;
-      if (k < nk) {
-        if (k + 2 < nk) loadA(u & 1, k + 2);
-        compute(u & 1, u % D);
-        if (k + D < nk) loadW(u % D, k + D);
-        if (k + 1 < nk) storeA((u + 1) & 1, (u + 1) & 1);
-        __syncthreads();
-      }
+      loadA(u & 1, min(k + 2, nk - 1));
+      compute(u & 1, u % D);
+      loadW(u % D, min(k + D, nk - 1));
+      storeA((u + 1) & 1, (u + 1) & 1);
+      __syncthreads();
     }
   }
 
@@ -291,6 +288,12 @@ hipError_t launch_cfg(int out_dtype, const GemmParams &g, int n_tiles, hipStream
 }  // namespace
 
 int stream_gemm_tile_rows(int w_dtype) { return w_dtype == MOE_DTYPE_FP8_E4M3 ? 128 : 256; }
+
+bool stream_gemm_fits(int w_dtype, int64_t K, int64_t I) {
+  const int eb = w_dtype == MOE_DTYPE_FP8_E4M3 ? 1 : 2;
+  // the gated kernel unrolls by 2 K-steps of 128 bytes, the down kernel by 4
+  return I % 128 == 0 && (K * eb / 128) % 2 == 0 && (I * eb / 128) % 4 == 0;
+}
 
 hipError_t launch_stream_gemm(int w_dtype, int out_dtype, GemmKind kind, const GemmParams &g, int n_tiles,
                               hipStream_t s) {
