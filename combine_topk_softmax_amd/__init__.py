@@ -16,7 +16,8 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe_gfx950.so")
+# MOE_LIBRARY may name another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("MOE_LIBRARY") or os.path.join(_HERE, "libmoe_gfx950.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 FORMAT_STANDARD, FORMAT_BATCHED_EXPERTS = 0, 1

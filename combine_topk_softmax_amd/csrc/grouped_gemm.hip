@@ -71,8 +71,12 @@ constexpr int kRowBytes = 128;             // one K-step: 128 bytes of every row
 constexpr int kTileBytes = 128 * kRowBytes; // 128 rows
 
 // Byte address of (row, byte b of the row's K-step) in a swizzled LDS tile.
+// gfx950 serves a 128-bit LDS access 16 lanes at a time over 64 banks (256
+// bytes): with 128-byte rows, rows r and r+1 share a bank row, so the 16-byte
+// chunk index is XORed with (row / 2) % 8 to give 16 consecutive rows of one
+// logical chunk 16 distinct bank groups.
 __device__ __forceinline__ int swz(int row, int b) {
-  return row * kRowBytes + ((((b >> 4) ^ (row & 7)) << 4) | (b & 15));
+  return row * kRowBytes + ((((b >> 4) ^ ((row >> 1) & 7)) << 4) | (b & 15));
 }
 
 template <int EB, bool GATED, bool OUT_BF16>

@@ -8,7 +8,7 @@
 // counts read on the device) -- organised around reading every weight byte
 // exactly once:
 //
-//  * one workgroup = one expert's rows (up to kTmax, masked by the device
+//  * one workgroup = one expert's rows (up to TMAX, masked by the device
 //    count in 16-row MFMA blocks) x a panel of weight rows, so an expert's
 //    weights are streamed once whatever its row count;
 //  * each of the 8 wavefronts owns its own 16-row weight blocks, which no
@@ -16,6 +16,10 @@
 //    registers, prefetched D K-steps ahead (no LDS round trip);
 //  * the activation rows, shared by all wavefronts, are staged through a
 //    double-buffered LDS tile (XOR-swizzled 16-byte chunks) two K-steps ahead;
+//  * the number of 16-row blocks is rounded up (1, 2, 4, 6, ...) and each
+//    value gets its own fully unrolled main loop, so no load, LDS access or
+//    MFMA sits behind a branch (branches around memory operations make the
+//    compiler wait for every outstanding load);
 //  * work items are dealt out XCD by XCD: consecutive items of one expert land
 //    on the same XCD, so its activation rows stay in that XCD's L2.
 //
@@ -53,8 +57,11 @@ struct Mfma16<1> {
   }
 };
 
+// Swizzled LDS address of byte b of a 128-byte tile row: the 16-byte chunk
+// index is XORed with (row / 2) % 8 so that 16 consecutive rows (one 128-bit
+// access pass over gfx950's 64 banks) hit 16 distinct bank groups.
 __device__ __forceinline__ int swz(int row, int b) {
-  return row * 128 + ((((b >> 4) ^ (row & 7)) << 4) | (b & 15));
+  return row * 128 + ((((b >> 4) ^ ((row >> 1) & 7)) << 4) | (b & 15));
 }
 
 template <typename F>
@@ -75,14 +82,13 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
   using MM = Mfma16<EB>;
   using frag = typename MM::frag;
   constexpr bool kScaled = EB == 1;
-  constexpr int kMB = TMAX / 16;            // MFMA row blocks
-  constexpr int kARows = TMAX / 64;         // A rows per thread per K-step
   constexpr int kFrag = 32 / MM::kSteps;    // bytes per lane per MFMA step
-  constexpr int U = D == 1 ? 2 : (D % 2 == 0 ? D : 2 * D);   // unroll = lcm(2, D)
+  constexpr int U = D % 2 == 0 ? D : 2 * D; // unroll = lcm(2, D); the host checks nk % U == 0
   static_assert(!GATED || NBW == 2, "a gated wave holds one gate and one up block");
+  static_assert(TMAX % 64 == 0 && TMAX <= 256, "row tile");
 
   __shared__ __attribute__((aligned(16))) uint8_t As[2][TMAX * 128];
-  __shared__ float Sa[2][TMAX];
+  __shared__ __attribute__((aligned(16))) float Sa[2][TMAX];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int total = *g.t.tile_count * n_tiles;
@@ -95,15 +101,14 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
   const int e = tile[0];
   const int64_t row0 = (int64_t)tile[1] + tile[2];
   const int T = tile[3];
-  const int nmb = (T + 15) >> 4;
   const int64_t row_bytes = g.Kred * EB;
   const int nk = (int)(row_bytes / 128);
   const int q = lane >> 4, r16 = lane & 15;
+  const int64_t kblocks = g.Kred / 128;
 
-  // ---- weight rows of this wavefront (NBW blocks of 16 rows)
+  // Weight rows of this wavefront: NBW blocks of 16 rows.
   const uint8_t *wsrc[NBW];
   const float *wscale[NBW];
-  const int64_t kblocks = g.Kred / 128;
 #pragma unroll
   for (int b = 0; b < NBW; ++b) {
     int64_t wrow0;
@@ -114,163 +119,189 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
     wsrc[b] = reinterpret_cast<const uint8_t *>(g.w) + ((int64_t)e * g.Nw + wrow0 + r16) * row_bytes + q * 32;
     wscale[b] = kScaled ? g.w_scale + ((int64_t)e * (g.Nw / 128) + wrow0 / 128) * kblocks : nullptr;
   }
-
-  // ---- activation rows this thread stages (row index in A, or -1)
+  // A row (in the activation tensor) of tile row r; rows past the count map to
+  // the last real row so that their loads share its cache lines.
+  auto a_row_of = [&](int r, bool &ok) -> int64_t {
+    const int rc = min(r, T - 1);
+    const int64_t s = row0 + rc;
+    ok = r < T;
+    if (!g.perm) return s;
+    const int f = g.perm[s];
+    if (f < 0 || f >= g.n_pairs) {
+      ok = false;
+      return 0;
+    }
+    return f / g.topk;
+  };
   const int ach = tid & 7;
-  int64_t arow[kARows];
-#pragma unroll
-  for (int i = 0; i < kARows; ++i) {
-    const int r = (tid >> 3) + 64 * i;
-    arow[i] = -2;                            // -2: not needed (beyond the last row block)
-    if (r < nmb * 16) {
-      arow[i] = -1;                          // -1: zero row (past the count)
-      if (r < T) {
-        const int64_t s = row0 + r;
-        int64_t a = s;
-        if (g.perm) {
-          const int f = g.perm[s];
-          a = (f >= 0 && f < g.n_pairs) ? f / g.topk : -1;
-        }
-        arow[i] = a;
-      }
-    }
-  }
-  int64_t srow = -1;                          // fp8: this thread's row scale source (tid < T)
-  if (kScaled && tid < T) {
-    const int64_t s = row0 + tid;
-    srow = s;
-    if (g.perm) {
-      const int f = g.perm[s];
-      srow = (f >= 0 && f < g.n_pairs) ? f / g.topk : -1;
-    }
-  }
   const uint8_t *abase = reinterpret_cast<const uint8_t *>(g.a) + ach * 16;
 
-  // Loads are unconditional (rows past the count read row 0, K-steps past the
-  // end re-read the last one) so that the loop body has no branches around
-  // memory operations; the zero mask is applied when the rows reach LDS.
-  uint4 ra[2][kARows];
-  float rsa[2] = {0.0f, 0.0f};
-  auto loadA = [&](int j, int ks) {
+  // The main loop for NMB blocks of 16 rows (NMB * 16 >= T): every load, LDS
+  // access and MFMA is unconditional.
+  auto body = [&]<int NMB>() {
+    constexpr int kPasses = (NMB * 16 + 63) / 64;   // A rows per thread per K-step
+    int64_t arow[kPasses];
+    bool aok[kPasses];
 #pragma unroll
-    for (int i = 0; i < kARows; ++i)
-      ra[j][i] = *reinterpret_cast<const uint4 *>(abase + (arow[i] >= 0 ? arow[i] : 0) * row_bytes +
-                                                   (int64_t)ks * 128);
-    if constexpr (kScaled) rsa[j] = g.a_scale[(srow >= 0 ? srow : 0) * kblocks + ks];
-  };
-  auto storeA = [&](int j, int st) {
-#pragma unroll
-    for (int i = 0; i < kARows; ++i) {
-      const int r = (tid >> 3) + 64 * i;
-      const uint4 v = arow[i] >= 0 ? ra[j][i] : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4 *>(&As[st][swz(r, ach * 16)]) = v;
-    }
-    if constexpr (kScaled)
-      if (tid < TMAX) Sa[st][tid] = srow >= 0 ? rsa[j] : 0.0f;
-  };
+    for (int i = 0; i < kPasses; ++i) arow[i] = a_row_of((tid >> 3) + 64 * i, aok[i]);
+    bool sok = false;
+    const int64_t srow = kScaled ? a_row_of(tid, sok) : 0;
 
-  uint4 wb[D][NBW][2];
-  float wsv[D][NBW];
-  auto loadW = [&](int j, int ks) {
+    uint4 ra[2][kPasses];
+    float rsa[2] = {0.0f, 0.0f};
+    auto loadA = [&](int j, int ks) {
 #pragma unroll
-    for (int b = 0; b < NBW; ++b) {
-      const uint4 *p = reinterpret_cast<const uint4 *>(wsrc[b] + (int64_t)ks * 128);
-      wb[j][b][0] = p[0];
-      wb[j][b][1] = p[1];
-      if constexpr (kScaled) wsv[j][b] = wscale[b][ks];
-    }
-  };
-
-  f32x4 acc[kMB][NBW];
+      for (int i = 0; i < kPasses; ++i)
+        ra[j][i] = *reinterpret_cast<const uint4 *>(abase + arow[i] * row_bytes + (int64_t)ks * 128);
+      if constexpr (kScaled) rsa[j] = g.a_scale[srow * kblocks + ks];
+    };
+    auto storeA = [&](int j, int st) {
 #pragma unroll
-  for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-    for (int b = 0; b < NBW; ++b) acc[mb][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-  auto compute = [&](int st, int j) {
-    const uint8_t *A = As[st];
-#pragma unroll
-    for (int mb = 0; mb < kMB; ++mb) {
-      if (mb < nmb) {  // uniform
-      const int ar = mb * 16 + r16;
-      f32x4 part[NBW];
+      for (int i = 0; i < kPasses; ++i) {
+        const int r = (tid >> 3) + 64 * i;
+        *reinterpret_cast<uint4 *>(&As[st][swz(r, ach * 16)]) = aok[i] ? ra[j][i] : make_uint4(0, 0, 0, 0);
+      }
       if constexpr (kScaled)
+        if (tid < TMAX) Sa[st][tid] = sok ? rsa[j] : 0.0f;
+    };
+
+    uint4 wb[D][NBW][2];
+    float wsv[D][NBW];
+    auto loadW = [&](int j, int ks) {
 #pragma unroll
-        for (int b = 0; b < NBW; ++b) part[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int b = 0; b < NBW; ++b) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(wsrc[b] + (int64_t)ks * 128);
+        wb[j][b][0] = p[0];
+        wb[j][b][1] = p[1];
+        if constexpr (kScaled) wsv[j][b] = wscale[b][ks];
+      }
+    };
+
+    f32x4 acc[NMB][NBW];
 #pragma unroll
-      for (int t = 0; t < MM::kSteps; ++t) {
-        const frag af = *reinterpret_cast<const frag *>(A + swz(ar, q * 32 + t * kFrag));
+    for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-        for (int b = 0; b < NBW; ++b) {
-          const frag bf = frag_at<frag>(wb[j][b], t);
-          if constexpr (kScaled)
-            part[b] = MM::mma(af, bf, part[b]);
+      for (int b = 0; b < NBW; ++b) acc[mb][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // One K-step of MFMAs; the next block's A fragments are read from LDS
+    // before the current block's MFMAs so that LDS latency hides behind them.
+    auto compute = [&](int st, int j) {
+      const uint8_t *A = As[st];
+      frag an[MM::kSteps];
+#pragma unroll
+      for (int t = 0; t < MM::kSteps; ++t)
+        an[t] = *reinterpret_cast<const frag *>(A + swz(r16, q * 32 + t * kFrag));
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        frag ac[MM::kSteps];
+#pragma unroll
+        for (int t = 0; t < MM::kSteps; ++t) ac[t] = an[t];
+        if (mb + 1 < NMB) {
+#pragma unroll
+          for (int t = 0; t < MM::kSteps; ++t)
+            an[t] = *reinterpret_cast<const frag *>(A + swz((mb + 1) * 16 + r16, q * 32 + t * kFrag));
+        }
+        f32x4 part[NBW];
+        if constexpr (kScaled)
+#pragma unroll
+          for (int b = 0; b < NBW; ++b) part[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int t = 0; t < MM::kSteps; ++t) {
+#pragma unroll
+          for (int b = 0; b < NBW; ++b) {
+            const frag bf = frag_at<frag>(wb[j][b], t);
+            if constexpr (kScaled)
+              part[b] = MM::mma(ac[t], bf, part[b]);
+            else
+              acc[mb][b] = MM::mma(ac[t], bf, acc[mb][b]);
+          }
+        }
+        if constexpr (kScaled) {
+          const float4 sa4 = *reinterpret_cast<const float4 *>(&Sa[st][mb * 16 + q * 4]);
+          const float sa[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int b = 0; b < NBW; ++b) acc[mb][b][i] += part[b][i] * (sa[i] * wsv[j][b]);
+          // Fold each block's partial sums here: without this the compiler
+          // sinks all blocks' scale FMAs to the end of the K-step and keeps
+          // every block's partial sums live at once.
+#pragma unroll
+          for (int b = 0; b < NBW; ++b) asm volatile("" : "+v"(acc[mb][b]));
+        }
+      }
+    };
+
+    // Pipeline: A two K-steps ahead (registers -> LDS), weights D ahead.
+    loadA(0, 0);
+    loadA(1, min(1, nk - 1));
+#pragma unroll
+    for (int j = 0; j < D; ++j) loadW(j, min(j, nk - 1));
+    storeA(0, 0);
+    __syncthreads();
+    for (int kb = 0; kb < nk; kb += U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = kb + u;
+        loadA(u & 1, min(k + 2, nk - 1));
+        compute(u & 1, u % D);
+        loadW(u % D, min(k + D, nk - 1));
+        storeA((u + 1) & 1, (u + 1) & 1);
+        __syncthreads();
+      }
+    }
+
+    // Epilogue: in a 16x16 block, lane holds column r16 of rows 4*q + i.
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = mb * 16 + q * 4 + i;
+        if (r >= T) continue;
+        const int64_t slot = row0 + r;
+        if constexpr (GATED) {
+          const float gt = acc[mb][0][i], up = acc[mb][1][i];
+          const float v = gt / (1.0f + expf(-gt)) * up;
+          const int64_t col = (int64_t)nt * 128 + wv * 16 + r16;
+          if constexpr (OUT_BF16)
+            reinterpret_cast<uint16_t *>(g.out)[slot * g.ldo + col] = f32_to_bf16_bits(v);
           else
-            acc[mb][b] = MM::mma(af, bf, acc[mb][b]);
-        }
-      }
-      if constexpr (kScaled) {
+            reinterpret_cast<float *>(g.out)[slot * g.ldo + col] = v;
+        } else {
+          const int64_t orow = g.out_perm ? g.out_perm[slot] : slot;
+          if (orow < 0 || (g.out_perm && orow >= g.n_pairs)) continue;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float sa = Sa[st][mb * 16 + q * 4 + i];
-#pragma unroll
-          for (int b = 0; b < NBW; ++b) acc[mb][b][i] += part[b][i] * (sa * wsv[j][b]);
+          for (int b = 0; b < NBW; ++b) {
+            const int64_t col = (int64_t)nt * (128 * NBW) + wv * (16 * NBW) + b * 16 + r16;
+            if constexpr (OUT_BF16)
+              reinterpret_cast<uint16_t *>(g.out)[orow * g.ldo + col] = f32_to_bf16_bits(acc[mb][b][i]);
+            else
+              reinterpret_cast<float *>(g.out)[orow * g.ldo + col] = acc[mb][b][i];
+          }
         }
-      }
       }
     }
   };
 
-  // ---- pipeline: A two K-steps ahead (registers -> LDS), weights D ahead.
-  // The host guarantees nk % U == 0.
-  loadA(0, 0);
-  loadA(1, min(1, nk - 1));
-#pragma unroll
-  for (int j = 0; j < D; ++j) loadW(j, min(j, nk - 1));
-  storeA(0, 0);
-  __syncthreads();
-
-  for (int kb = 0; kb < nk; kb += U) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k = kb + u;
-      loadA(u & 1, min(k + 2, nk - 1));
-      compute(u & 1, u % D);
-      loadW(u % D, min(k + D, nk - 1));
-      storeA((u + 1) & 1, (u + 1) & 1);
-      __syncthreads();
-    }
-  }
-
-  // ---- epilogue: 16x16 block, lane holds column r16, rows 4*q + i.
-#pragma unroll
-  for (int mb = 0; mb < kMB; ++mb) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = mb * 16 + q * 4 + i;
-      if (r >= T) continue;
-      const int64_t slot = row0 + r;
-      if constexpr (GATED) {
-        const float gt = acc[mb][0][i], up = acc[mb][1][i];
-        const float v = gt / (1.0f + expf(-gt)) * up;
-        const int64_t col = (int64_t)nt * 128 + wv * 16 + r16;
-        if constexpr (OUT_BF16)
-          reinterpret_cast<uint16_t *>(g.out)[slot * g.ldo + col] = f32_to_bf16_bits(v);
-        else
-          reinterpret_cast<float *>(g.out)[slot * g.ldo + col] = v;
-      } else {
-        const int64_t orow = g.out_perm ? g.out_perm[slot] : slot;
-        if (orow < 0 || (g.out_perm && orow >= g.n_pairs)) continue;
-#pragma unroll
-        for (int b = 0; b < NBW; ++b) {
-          const int64_t col = (int64_t)nt * (128 * NBW) + wv * (16 * NBW) + b * 16 + r16;
-          if constexpr (OUT_BF16)
-            reinterpret_cast<uint16_t *>(g.out)[orow * g.ldo + col] = f32_to_bf16_bits(acc[mb][b][i]);
-          else
-            reinterpret_cast<float *>(g.out)[orow * g.ldo + col] = acc[mb][b][i];
+  // Row blocks rounded up to 1, 2, 4, 6, ... (one specialised loop each).
+  const int nmb = (T + 15) >> 4;
+  const int nq = nmb <= 1 ? 1 : (nmb + 1) & ~1;
+  switch (nq) {
+    case 1: body.template operator()<1>(); break;
+    case 2: body.template operator()<2>(); break;
+    case 4: body.template operator()<4>(); break;
+    case 6: body.template operator()<6>(); break;
+    case 8: body.template operator()<8>(); break;
+    default:
+      if constexpr (TMAX >= 256) {
+        switch (nq) {
+          case 10: body.template operator()<10>(); break;
+          case 12: body.template operator()<12>(); break;
+          case 14: body.template operator()<14>(); break;
+          default: body.template operator()<16>(); break;
         }
       }
-    }
+      break;
   }
 }
 
@@ -289,20 +320,39 @@ hipError_t launch_cfg(int out_dtype, const GemmParams &g, int n_tiles, hipStream
 
 int stream_gemm_tile_rows(int w_dtype) { return w_dtype == MOE_DTYPE_FP8_E4M3 ? 128 : 256; }
 
+// Prefetch depths (K-steps of weights in flight per wavefront), per dtype so
+// that accumulators, staging and prefetch fit 256 registers.
+#ifndef MOE_STREAM_GATED_D_BF16
+#define MOE_STREAM_GATED_D_BF16 2
+#endif
+#ifndef MOE_STREAM_DOWN_D_BF16
+#define MOE_STREAM_DOWN_D_BF16 4
+#endif
+#ifndef MOE_STREAM_GATED_D_FP8
+#define MOE_STREAM_GATED_D_FP8 2
+#endif
+#ifndef MOE_STREAM_DOWN_D_FP8
+#define MOE_STREAM_DOWN_D_FP8 4
+#endif
+
+constexpr int unroll_of(int d) { return d % 2 == 0 ? d : 2 * d; }
+
 bool stream_gemm_fits(int w_dtype, int64_t K, int64_t I) {
-  const int eb = w_dtype == MOE_DTYPE_FP8_E4M3 ? 1 : 2;
-  // the gated kernel unrolls by 2 K-steps of 128 bytes, the down kernel by 4
-  return I % 128 == 0 && (K * eb / 128) % 2 == 0 && (I * eb / 128) % 4 == 0;
+  const bool fp8 = w_dtype == MOE_DTYPE_FP8_E4M3;
+  const int eb = fp8 ? 1 : 2;
+  const int ug = unroll_of(fp8 ? MOE_STREAM_GATED_D_FP8 : MOE_STREAM_GATED_D_BF16);
+  const int ud = unroll_of(fp8 ? MOE_STREAM_DOWN_D_FP8 : MOE_STREAM_DOWN_D_BF16);
+  return I % 128 == 0 && (K * eb / 128) % ug == 0 && (I * eb / 128) % ud == 0;
 }
 
 hipError_t launch_stream_gemm(int w_dtype, int out_dtype, GemmKind kind, const GemmParams &g, int n_tiles,
                               hipStream_t s) {
   const bool fp8 = w_dtype == MOE_DTYPE_FP8_E4M3;
   if (kind == kGemmGatedAct)
-    return fp8 ? launch_cfg<1, true, 2, 2, 128>(out_dtype, g, n_tiles, s)
-               : launch_cfg<2, true, 2, 2, 256>(out_dtype, g, n_tiles, s);
-  return fp8 ? launch_cfg<1, false, 1, 4, 128>(out_dtype, g, n_tiles, s)
-             : launch_cfg<2, false, 1, 4, 256>(out_dtype, g, n_tiles, s);
+    return fp8 ? launch_cfg<1, true, 2, MOE_STREAM_GATED_D_FP8, 128>(out_dtype, g, n_tiles, s)
+               : launch_cfg<2, true, 2, MOE_STREAM_GATED_D_BF16, 256>(out_dtype, g, n_tiles, s);
+  return fp8 ? launch_cfg<1, false, 1, MOE_STREAM_DOWN_D_FP8, 128>(out_dtype, g, n_tiles, s)
+             : launch_cfg<2, false, 1, MOE_STREAM_DOWN_D_BF16, 256>(out_dtype, g, n_tiles, s);
 }
 
 }  // namespace moe
