@@ -25,6 +25,7 @@ DTYPE_F32, DTYPE_BF16, DTYPE_FP8_E4M3 = 0, 1, 2
 QUANT_NONE, QUANT_FP8_TOKEN_GROUP_128 = 0, 1
 SCORING_SOFTMAX, SCORING_SIGMOID = 0, 1
 DEVICE_BAD_EXPERT_ID, DEVICE_CAPACITY_OVERFLOW = 1, 2
+WEIGHTS_ROW_MAJOR, WEIGHTS_PACKED = 0, 1
 NUM_STAGE_EVENTS = 6
 
 
@@ -42,6 +43,7 @@ class Problem(C.Structure):
         ("format", C.c_int32), ("act_dtype", C.c_int32), ("w_dtype", C.c_int32),
         ("act_quant", C.c_int32), ("scoring", C.c_int32), ("renormalize", C.c_int32),
         ("activation", C.c_int32), ("apply_router_weight_on_input", C.c_int32),
+        ("weight_layout", C.c_int32), ("reserved", C.c_int32),
         ("expert_map", C.c_void_p),
     ]
 
@@ -67,7 +69,7 @@ class WsLayout(C.Structure):
 
 
 EXPORTS = ("moe_status_str", "moe_version", "moe_validate", "moe_workspace_size", "moe_workspace_layout",
-           "moe_route", "moe_prepare", "moe_experts", "moe_finalize", "moe_shared_expert", "moe_forward")
+           "moe_pack_weights", "moe_route", "moe_prepare", "moe_experts", "moe_finalize", "moe_shared_expert", "moe_forward")
 
 _lib = None
 
@@ -87,6 +89,7 @@ def load_library(path: str = LIB_PATH):
         "moe_validate": [P(Problem)],
         "moe_workspace_size": [P(Problem), P(C.c_size_t)],
         "moe_workspace_layout": [P(Problem), P(WsLayout)],
+        "moe_pack_weights": [P(Problem), P(Weights), vp, vp, vp],
         "moe_route": [P(Problem), vp, vp, vp, vp],
         "moe_prepare": [P(Problem), vp, vp, vp, vp, vp, vp, C.c_size_t, vp],
         "moe_experts": [P(Problem), vp, vp, P(Weights), vp, vp, vp, C.c_size_t, vp],
@@ -131,11 +134,11 @@ def _ws(ws: torch.Tensor):
 
 def make_problem(E, M, N, K, topk, *, format=FORMAT_STANDARD, act_dtype=DTYPE_BF16, w_dtype=DTYPE_BF16,
                  act_quant=QUANT_NONE, scoring=SCORING_SOFTMAX, renormalize=False,
-                 max_tokens_per_expert=0, align=0, shared_N=0) -> Problem:
+                 max_tokens_per_expert=0, align=0, shared_N=0, weight_layout=WEIGHTS_ROW_MAJOR) -> Problem:
     return Problem(E=E, M=M, N=N, K=K, topk=topk, max_tokens_per_expert=max_tokens_per_expert, align=align,
                    shared_N=shared_N, format=format, act_dtype=act_dtype, w_dtype=w_dtype,
                    act_quant=act_quant, scoring=scoring, renormalize=int(renormalize), activation=0,
-                   apply_router_weight_on_input=0, expert_map=None)
+                   apply_router_weight_on_input=0, weight_layout=weight_layout, reserved=0, expert_map=None)
 
 
 def validate(p: Problem) -> int:
@@ -156,6 +159,20 @@ def workspace_layout(p: Problem) -> WsLayout:
 
 def empty_workspace(p: Problem, device="cuda") -> torch.Tensor:
     return torch.empty(workspace_size(p), dtype=torch.uint8, device=device)
+
+
+def moe_pack_weights(p: Problem, w1, w2, w1_packed, w2_packed, stream=None):
+    """One-time reordering of row-major w1 / w2 into the packed layout."""
+    src = _weights(w1, None, w2, None)
+    _check(load_library().moe_pack_weights(C.byref(p), C.byref(src), _ptr(w1_packed), _ptr(w2_packed),
+                                           _stream(stream)), "moe_pack_weights")
+
+
+def pack_weights(p: Problem, w1, w2, stream=None):
+    """Packed copies of w1 / w2 (new tensors of the same shape and dtype)."""
+    w1p, w2p = torch.empty_like(w1), torch.empty_like(w2)
+    moe_pack_weights(p, w1, w2, w1p, w2p, stream)
+    return w1p, w2p
 
 
 def moe_route(p: Problem, logits, topk_weights, topk_ids, stream=None):

@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_gfx950.so")
-SOURCES = ["moe_api.hip", "route.hip", "dispatch.hip", "grouped_gemm.hip", "stream_gemm.hip", "combine.hip"]
+SOURCES = ["moe_api.hip", "route.hip", "dispatch.hip", "grouped_gemm.hip", "stream_gemm.hip", "combine.hip", "pack.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -22,13 +22,33 @@ FLAGS = [
 
 
 def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    """Compile every source to an object in parallel, then link the library."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+
+    compile_flags = [f for f in FLAGS if f not in ("-shared", "-Wl,-z,defs")]
+    tmpdir = tempfile.mkdtemp(prefix="moe_build_")
+    objs = []
+
+    def one(src):
+        obj = os.path.join(tmpdir, os.path.splitext(src)[0] + ".o")
+        cmd = [HIPCC, *compile_flags, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.check_call(cmd)
+        return obj
+
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(one, SOURCES))
     tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], *srcs, "-o", tmp]
+    link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,-z,defs", *objs, "-o", tmp]
     if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.check_call(cmd)
+        print(" ".join(link), flush=True)
+    subprocess.check_call(link)
     os.replace(tmp, out)
+    for o in objs:
+        os.remove(o)
+    os.rmdir(tmpdir)
     return out
 
 

@@ -79,7 +79,7 @@ __device__ __forceinline__ int swz(int row, int b) {
   return row * kRowBytes + ((((b >> 4) ^ ((row >> 1) & 7)) << 4) | (b & 15));
 }
 
-template <int EB, bool GATED, bool OUT_BF16>
+template <int EB, bool GATED, bool OUT_BF16, bool PACKED>
 __global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmParams g) {
   using MM = Mfma<EB>;
   using frag = typename MM::frag;
@@ -111,6 +111,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmParams g) {
   const int64_t row_bytes = g.Kred * EB;
   const int nk = (int)(row_bytes / kRowBytes);
   const int chunk = tid & 7;
+  const PackedGeom pg = packed_geom(g.Nw, row_bytes, GATED);
+  const int64_t kstride = PACKED ? packed_kstep_stride(pg) : kRowBytes;   // weight bytes between K-steps
 
   // Source rows of this thread's 4 A chunks and 4 B chunks per K-step.
   const uint8_t *a_src[4];
@@ -140,7 +142,10 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmParams g) {
       wrow = r < 64 ? (int64_t)nt * 64 + r : g.half_n + (int64_t)nt * 64 + (r - 64);
     else
       wrow = (int64_t)nt * 128 + r;
-    b_src[i] = reinterpret_cast<const uint8_t *>(g.w) + ((int64_t)e * g.Nw + wrow) * row_bytes + chunk * 16;
+    if (PACKED)
+      b_src[i] = reinterpret_cast<const uint8_t *>(g.w) + packed_piece(pg, e, wrow, 0, chunk);
+    else
+      b_src[i] = reinterpret_cast<const uint8_t *>(g.w) + ((int64_t)e * g.Nw + wrow) * row_bytes + chunk * 16;
   }
   // fp8: per-row activation scale (thread tid < 128 owns row tid), per-block weight scales.
   const float *sa_src = g.a_scale;
@@ -186,11 +191,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmParams g) {
   uint4 ra[4], rb[4];
   float sa_reg = 0.0f;
   auto gload = [&](int ks) {
-    const int64_t off = (int64_t)ks * kRowBytes;
+    const int64_t off = (int64_t)ks * kRowBytes;   // activation bytes
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       ra[i] = *reinterpret_cast<const uint4 *>(a_src[i] + off);
-      rb[i] = *reinterpret_cast<const uint4 *>(b_src[i] + off);
+      rb[i] = *reinterpret_cast<const uint4 *>(b_src[i] + (int64_t)ks * kstride);
     }
     if constexpr (kScaled) sa_reg = sa_src[ks];
   };
@@ -304,10 +309,18 @@ template <int EB, bool GATED>
 hipError_t launch_typed(int out_dtype, const GemmParams &g, int n_tiles, hipStream_t s) {
   const int m_tiles = g.t.dense_rows > 0 ? (g.t.dense_rows + 127) / 128 : g.t.max_tiles;
   dim3 grid((unsigned)(m_tiles * n_tiles)), block(256);
-  if (out_dtype == MOE_DTYPE_BF16)
-    grouped_gemm_kernel<EB, GATED, true><<<grid, block, 0, s>>>(g);
-  else
-    grouped_gemm_kernel<EB, GATED, false><<<grid, block, 0, s>>>(g);
+  const bool bf = out_dtype == MOE_DTYPE_BF16;
+  if (g.w_packed) {
+    if (bf)
+      grouped_gemm_kernel<EB, GATED, true, true><<<grid, block, 0, s>>>(g);
+    else
+      grouped_gemm_kernel<EB, GATED, false, true><<<grid, block, 0, s>>>(g);
+  } else {
+    if (bf)
+      grouped_gemm_kernel<EB, GATED, true, false><<<grid, block, 0, s>>>(g);
+    else
+      grouped_gemm_kernel<EB, GATED, false, false><<<grid, block, 0, s>>>(g);
+  }
   return hipGetLastError();
 }
 

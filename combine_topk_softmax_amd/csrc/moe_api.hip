@@ -20,6 +20,8 @@ int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
 int64_t act_elem_bytes(int32_t dt) { return dt == MOE_DTYPE_F32 ? 4 : 2; }
 
+int64_t w_elem_bytes(int32_t dt) { return dt == MOE_DTYPE_F32 ? 4 : dt == MOE_DTYPE_BF16 ? 2 : 1; }
+
 bool fp8_path(const moe_problem &p) { return p.w_dtype == MOE_DTYPE_FP8_E4M3; }
 
 // Checks of _moe_problem_size, the activation's 2:1 width rule,
@@ -41,6 +43,8 @@ moe_status validate(const moe_problem *pp) {
   if (p.act_quant != MOE_QUANT_NONE && p.act_quant != MOE_QUANT_FP8_TOKEN_GROUP_128) return MOE_ERR_INVALID_ARG;
   if (p.activation != MOE_ACTIVATION_SILU) return MOE_ERR_UNSUPPORTED;
   if (p.apply_router_weight_on_input != 0 || p.expert_map != nullptr) return MOE_ERR_UNSUPPORTED;
+  if (p.reserved != 0) return MOE_ERR_INVALID_ARG;
+  if (p.weight_layout != MOE_WEIGHTS_ROW_MAJOR && p.weight_layout != MOE_WEIGHTS_PACKED) return MOE_ERR_INVALID_ARG;
   if (p.E > kMaxExperts || p.topk > 64) return MOE_ERR_UNSUPPORTED;
   const int64_t I = p.N / 2;
   if (p.K % 128 != 0 || I % 64 != 0) return MOE_ERR_UNSUPPORTED;
@@ -51,6 +55,7 @@ moe_status validate(const moe_problem *pp) {
     if (p.act_quant != MOE_QUANT_NONE || p.w_dtype != p.act_dtype) return MOE_ERR_UNSUPPORTED;
   }
   if (p.shared_N > 0 && (p.shared_N % 128 != 0 || fp8_path(p))) return MOE_ERR_UNSUPPORTED;
+  if (p.weight_layout == MOE_WEIGHTS_PACKED && I % 128 != 0) return MOE_ERR_UNSUPPORTED;
   const int64_t align = p.align > 0 ? p.align : 1;
   if (align > 4096) return MOE_ERR_UNSUPPORTED;
   const int64_t pairs = p.M * p.topk;
@@ -183,6 +188,7 @@ moe_status do_experts(const moe_problem &p, const void *a, const float *a_scale,
   g1.out = at<void>(ws, L.act);
   g1.ldo = I;
   g1.half_n = I;
+  g1.w_packed = p.weight_layout == MOE_WEIGHTS_PACKED;
   g1.t = gt;
   if (streaming)
     MOE_HIP(launch_stream_gemm(p.w_dtype, fp8 ? MOE_DTYPE_F32 : p.act_dtype, kGemmGatedAct, g1,
@@ -210,6 +216,7 @@ moe_status do_experts(const moe_problem &p, const void *a, const float *a_scale,
   g2.ldo = p.K;
   g2.out_perm = perm;
   g2.half_n = 0;
+  g2.w_packed = p.weight_layout == MOE_WEIGHTS_PACKED;
   g2.t = gt;
   if (streaming)
     MOE_HIP(launch_stream_gemm(p.w_dtype, p.act_dtype, kGemmDown, g2, (int)(p.K / 128), s));
@@ -288,6 +295,21 @@ moe_status moe_workspace_size(const moe_problem *p, size_t *bytes) {
   moe_status st = moe_workspace_layout(p, &L);
   if (st == MOE_OK) *bytes = L.total_bytes;
   return st;
+}
+
+moe_status moe_pack_weights(const moe_problem *p, const moe_weights *src, void *w1_packed,
+                            void *w2_packed, hipStream_t stream) {
+  if (!p) return MOE_ERR_INVALID_ARG;
+  moe_problem q = *p;
+  q.weight_layout = MOE_WEIGHTS_PACKED;   // the target layout's constraints apply
+  moe_status st = validate(&q);
+  if (st != MOE_OK) return st;
+  if (!src || !src->w1 || !src->w2 || !w1_packed || !w2_packed) return MOE_ERR_INVALID_ARG;
+  if (w1_packed == src->w1 || w2_packed == src->w2) return MOE_ERR_INVALID_ARG;
+  const int64_t eb = w_elem_bytes(p->w_dtype), I = p->N / 2;
+  MOE_HIP(launch_pack_weights(src->w1, w1_packed, p->E, p->N, p->K * eb, true, stream));
+  MOE_HIP(launch_pack_weights(src->w2, w2_packed, p->E, p->K, I * eb, false, stream));
+  return MOE_OK;
 }
 
 moe_status moe_route(const moe_problem *p, const float *logits, float *topk_weights,

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "../../include/moe.h"
 
 namespace moe {
@@ -84,6 +86,49 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
+// ------------------------------------------------------- packed weights
+// MOE_WEIGHTS_PACKED: weight rows are grouped in panels of 128 rows ("gated"
+// w1: gate rows [128 P, 128 P + 128) together with the matching up rows;
+// "down" w2: rows [128 P, 128 P + 128)).  For each (expert, panel, K-step of
+// 128 bytes, wavefront w of 8, block b of nbw, piece p of 2, lane l of 64) one
+// 16-byte piece holds bytes [32 (l / 16) + 16 p, +16) of the K-step of panel
+// row 16 w + l % 16 of block b.  So a wavefront's K-step (nbw x 2 KB) is
+// contiguous and every 1 KB of it is exactly one 64-lane 16-byte load in MFMA
+// fragment order.  Sizes are those of the row-major tensors.
+struct PackedGeom {
+  int64_t half;      // rows per block kind: I (gated) or Nw (down)
+  int64_t n_panels;  // half / 128
+  int64_t nk;        // K-steps per row: row_bytes / 128
+  int nbw;           // 2 (gated: gate + up) or 1 (down)
+};
+
+__host__ __device__ inline PackedGeom packed_geom(int64_t Nw, int64_t row_bytes, bool gated) {
+  PackedGeom g;
+  g.half = gated ? Nw / 2 : Nw;
+  g.n_panels = g.half / 128;
+  g.nk = row_bytes / 128;
+  g.nbw = gated ? 2 : 1;
+  return g;
+}
+
+// Byte offset of the 16-byte piece holding bytes [16 c, 16 c + 16) of K-step
+// ks of row `row` of expert e.
+__host__ __device__ inline int64_t packed_piece(const PackedGeom &g, int64_t e, int64_t row, int64_t ks, int c) {
+  int b = 0;
+  int64_t rr = row;
+  if (g.nbw == 2 && row >= g.half) {
+    b = 1;
+    rr = row - g.half;
+  }
+  const int64_t panel = rr / 128;
+  const int w = (int)((rr % 128) / 16), r16 = (int)(rr % 16);
+  const int lane = (c >> 1) * 16 + r16, p = c & 1;
+  return ((((((e * g.n_panels + panel) * g.nk + ks) * 8 + w) * g.nbw + b) * 2 + p) * 64 + lane) * 16;
+}
+
+// Bytes between consecutive K-steps of one row in the packed layout.
+__host__ __device__ inline int64_t packed_kstep_stride(const PackedGeom &g) { return (int64_t)g.nbw * 16384; }
+
 // ------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; shapes are validated by the
 // C ABI before these are called.
@@ -114,6 +159,7 @@ struct GemmParams {
   int64_t ldo;
   const int32_t *out_perm;    // down GEMM: slot -> output row; NULL: row = slot
   int64_t half_n;             // gated: I (up rows start here)
+  int w_packed;               // weights in MOE_WEIGHTS_PACKED order
   GemmTiles t;
 };
 
@@ -142,6 +188,8 @@ int stream_gemm_tile_rows(int w_dtype);
 bool stream_gemm_fits(int w_dtype, int64_t K, int64_t I);
 hipError_t launch_stream_gemm(int w_dtype, int out_dtype, GemmKind kind, const GemmParams &g, int n_tiles,
                               hipStream_t s);
+hipError_t launch_pack_weights(const void *src, void *dst, int64_t E, int64_t Nw, int64_t row_bytes, bool gated,
+                               hipStream_t s);
 hipError_t launch_combine(const moe_problem &p, const void *fused_out, const float *topk_w,
                           const int32_t *inv, void *out, hipStream_t s);
 

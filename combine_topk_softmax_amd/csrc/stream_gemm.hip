@@ -77,7 +77,22 @@ __device__ __forceinline__ F frag_at(const uint4 (&v)[2], int t) {
 
 constexpr int kThreads = 512;
 
-template <int EB, bool GATED, bool OUT_BF16, int NBW, int D, int TMAX>
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte weight load; packed weights stream once in whole cache lines, so
+// they are read non-temporally (the row-major pattern touches half lines per
+// instruction and is faster through the cache).
+template <bool NT>
+__device__ __forceinline__ uint4 load_w16(const uint8_t *p) {
+  if constexpr (NT) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  } else {
+    return *reinterpret_cast<const uint4 *>(p);
+  }
+}
+
+template <int EB, bool GATED, bool OUT_BF16, int NBW, int D, int TMAX, bool PACKED>
 __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams g, int n_tiles) {
   using MM = Mfma16<EB>;
   using frag = typename MM::frag;
@@ -106,7 +121,11 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
   const int q = lane >> 4, r16 = lane & 15;
   const int64_t kblocks = g.Kred / 128;
 
-  // Weight rows of this wavefront: NBW blocks of 16 rows.
+  // Weight rows of this wavefront: NBW blocks of 16 rows.  A lane reads two
+  // 16-byte pieces per block and K-step: bytes [32 q, 32 q + 32) of its row.
+  const PackedGeom pg = packed_geom(g.Nw, row_bytes, GATED);
+  const int64_t kstride = PACKED ? packed_kstep_stride(pg) : 128;   // bytes between K-steps
+  constexpr int64_t pstride = PACKED ? 1024 : 16;                    // bytes between the two pieces
   const uint8_t *wsrc[NBW];
   const float *wscale[NBW];
 #pragma unroll
@@ -116,7 +135,10 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
       wrow0 = (b ? g.half_n : 0) + (int64_t)nt * 128 + wv * 16;
     else
       wrow0 = (int64_t)nt * (128 * NBW) + wv * (16 * NBW) + b * 16;
-    wsrc[b] = reinterpret_cast<const uint8_t *>(g.w) + ((int64_t)e * g.Nw + wrow0 + r16) * row_bytes + q * 32;
+    if (PACKED)
+      wsrc[b] = reinterpret_cast<const uint8_t *>(g.w) + packed_piece(pg, e, wrow0 + r16, 0, 2 * q);
+    else
+      wsrc[b] = reinterpret_cast<const uint8_t *>(g.w) + ((int64_t)e * g.Nw + wrow0 + r16) * row_bytes + q * 32;
     wscale[b] = kScaled ? g.w_scale + ((int64_t)e * (g.Nw / 128) + wrow0 / 128) * kblocks : nullptr;
   }
   // A row (in the activation tensor) of tile row r; rows past the count map to
@@ -170,9 +192,9 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
     auto loadW = [&](int j, int ks) {
 #pragma unroll
       for (int b = 0; b < NBW; ++b) {
-        const uint4 *p = reinterpret_cast<const uint4 *>(wsrc[b] + (int64_t)ks * 128);
-        wb[j][b][0] = p[0];
-        wb[j][b][1] = p[1];
+        const uint8_t *p = wsrc[b] + (int64_t)ks * kstride;
+        wb[j][b][0] = load_w16<PACKED>(p);
+        wb[j][b][1] = load_w16<PACKED>(p + pstride);
         if constexpr (kScaled) wsv[j][b] = wscale[b][ks];
       }
     };
@@ -309,10 +331,18 @@ template <int EB, bool GATED, int NBW, int D, int TMAX>
 hipError_t launch_cfg(int out_dtype, const GemmParams &g, int n_tiles, hipStream_t s) {
   const int64_t items = (int64_t)g.t.max_tiles * n_tiles;
   dim3 grid((unsigned)(((items + 7) / 8) * 8)), block(kThreads);
-  if (out_dtype == MOE_DTYPE_BF16)
-    stream_gemm_kernel<EB, GATED, true, NBW, D, TMAX><<<grid, block, 0, s>>>(g, n_tiles);
-  else
-    stream_gemm_kernel<EB, GATED, false, NBW, D, TMAX><<<grid, block, 0, s>>>(g, n_tiles);
+  const bool bf = out_dtype == MOE_DTYPE_BF16;
+  if (g.w_packed) {
+    if (bf)
+      stream_gemm_kernel<EB, GATED, true, NBW, D, TMAX, true><<<grid, block, 0, s>>>(g, n_tiles);
+    else
+      stream_gemm_kernel<EB, GATED, false, NBW, D, TMAX, true><<<grid, block, 0, s>>>(g, n_tiles);
+  } else {
+    if (bf)
+      stream_gemm_kernel<EB, GATED, true, NBW, D, TMAX, false><<<grid, block, 0, s>>>(g, n_tiles);
+    else
+      stream_gemm_kernel<EB, GATED, false, NBW, D, TMAX, false><<<grid, block, 0, s>>>(g, n_tiles);
+  }
   return hipGetLastError();
 }
 

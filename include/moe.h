@@ -64,6 +64,13 @@ enum { MOE_QUANT_NONE = 0, MOE_QUANT_FP8_TOKEN_GROUP_128 = 1 };
 enum { MOE_SCORING_SOFTMAX = 0, MOE_SCORING_SIGMOID = 1 };
 enum { MOE_ACTIVATION_SILU = 0 };
 
+/* Weight layouts.  ROW_MAJOR is w1 [E, N, K] / w2 [E, K, N/2] as above.
+ * PACKED is the same bytes reordered by moe_pack_weights so that each
+ * wavefront of the weight-streaming GEMM reads one contiguous 4 KB block per
+ * K-step (128 bytes of 16 rows, in MFMA fragment order).  The packed layout
+ * is internal to this library version (moe_version) and needs (N/2) % 128 == 0. */
+enum { MOE_WEIGHTS_ROW_MAJOR = 0, MOE_WEIGHTS_PACKED = 1 };
+
 /* Bits of the device status word. */
 enum { MOE_DEVICE_BAD_EXPERT_ID = 1, MOE_DEVICE_CAPACITY_OVERFLOW = 2 };
 
@@ -90,6 +97,8 @@ typedef struct moe_problem {
   int32_t renormalize;           /* divide the k weights by their sum          */
   int32_t activation;            /* MOE_ACTIVATION_SILU only                  */
   int32_t apply_router_weight_on_input; /* must be 0                          */
+  int32_t weight_layout;         /* MOE_WEIGHTS_* of the expert weights        */
+  int32_t reserved;              /* must be 0                                  */
   const int32_t *expert_map;     /* must be NULL (global == local experts)    */
 } moe_problem;
 
@@ -168,6 +177,14 @@ moe_status moe_validate(const moe_problem *p);
  * modular_kernel.py page; one region per intermediate, none shared). */
 moe_status moe_workspace_size(const moe_problem *p, size_t *bytes);
 moe_status moe_workspace_layout(const moe_problem *p, moe_ws_layout *out);
+
+/* One-time reordering of row-major expert weights into MOE_WEIGHTS_PACKED
+ * (done once when weights are loaded, not per step).  src holds row-major
+ * w1 / w2 (the problem's weight_layout is ignored); w1_packed and w2_packed
+ * receive the same number of bytes each.  Scales are not reordered.  The
+ * buffers must not overlap their sources. */
+moe_status moe_pack_weights(const moe_problem *p, const moe_weights *src, void *w1_packed,
+                            void *w2_packed, hipStream_t stream);
 
 /* [Router]: logits [M, E] fp32 -> topk_weights [M, topk] fp32 and topk_ids
  * [M, topk] int32 (the topk_weights / topk_ids that

@@ -47,7 +47,7 @@ _LAYOUT_PROBE = r"""
 int main(void) {
   printf("moe_problem %zu\n", sizeof(moe_problem));
   F(moe_problem, E) F(moe_problem, max_tokens_per_expert) F(moe_problem, shared_N) F(moe_problem, format)
-  F(moe_problem, apply_router_weight_on_input) F(moe_problem, expert_map)
+  F(moe_problem, apply_router_weight_on_input) F(moe_problem, weight_layout) F(moe_problem, expert_map)
   printf("moe_weights %zu\n", sizeof(moe_weights));
   printf("moe_shared %zu\n", sizeof(moe_shared));
   F(moe_shared, output_ready)
@@ -136,6 +136,11 @@ def test_validation_status_codes():
     p = moe.make_problem(**base)
     p.scoring = 7
     assert moe.validate(p) == moe.MOE_ERR_INVALID_ARG
+    p = moe.make_problem(**base, weight_layout=5)
+    assert moe.validate(p) == moe.MOE_ERR_INVALID_ARG
+    p = moe.make_problem(**dict(base, N=2 * 192), weight_layout=moe.WEIGHTS_PACKED)   # packed panels need I % 128
+    assert moe.validate(p) == moe.MOE_ERR_UNSUPPORTED
+    assert moe.validate(moe.make_problem(**dict(base, N=2 * 192))) == moe.MOE_OK
 
 
 def test_host_errors_need_no_gpu():
@@ -155,6 +160,10 @@ def test_host_errors_need_no_gpu():
     assert L.moe_forward(C.byref(ps), fake, fake, C.byref(w), fake, None, fake, 1 << 40, None, None) \
         == moe.MOE_ERR_INVALID_ARG
     assert L.moe_shared_expert(C.byref(p), fake, fake, fake, fake, fake, ws_size, None) == moe.MOE_ERR_INVALID_ARG
+    src = moe.Weights(0x1000, None, 0x2000, None)
+    assert L.moe_pack_weights(C.byref(p), C.byref(src), None, fake, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_weights(C.byref(p), C.byref(src), C.c_void_p(0x1000), C.c_void_p(0x3000), None) \
+        == moe.MOE_ERR_INVALID_ARG                                                   # in place
     # M == 0: nothing to do, nothing launched
     p0 = moe.make_problem(E=8, M=0, N=256, K=256, topk=2)
     assert L.moe_route(C.byref(p0), None, None, None, None) == moe.MOE_OK

@@ -428,3 +428,56 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         assert torch.equal(out, e_out), it
         assert torch.equal(sout, e_sout), it
+
+
+# ---------------------------------------------------------------- packed weights
+
+PACK_CASES = {
+    "bf16_stream": WORKLOADS["mixtral_bf16"].replace(M=300, K=384, I=256, E=7, topk=3, renormalize=False,
+                                                     logits_dist="normal"),
+    "bf16_tiled": WORKLOADS["mixtral_bf16"].replace(M=1200, K=256, I=256, E=4, topk=2, renormalize=False,
+                                                    logits_dist="normal"),
+    "fp8_batched_stream": SMALL["fp8_batched"],
+    "fp8_standard_stream": SMALL["fp8_standard"],
+    "fp32_tiled": WORKLOADS["tiny_fp32"],
+}
+
+
+@pytest.mark.parametrize("name", list(PACK_CASES))
+def test_packed_weights_give_identical_results(name):
+    """The packed layout only moves bytes: the layer's output is bitwise the same."""
+    wl = PACK_CASES[name]
+    d = U.to_cuda(make_inputs(wl, seed=24, device="cpu"))
+    ref, _, _, p = U.run_forward(wl, d)
+    pp = U.problem(wl, weight_layout=moe.WEIGHTS_PACKED)
+    w1p, w2p = moe.pack_weights(pp, d["w1"], d["w2"])
+    torch.cuda.synchronize()
+    # packing permutes bytes within each tensor
+    for a, b in ((d["w1"], w1p), (d["w2"], w2p)):
+        va, vb = a.view(torch.uint8).flatten(), b.view(torch.uint8).flatten()
+        assert torch.equal(torch.bincount(va.long(), minlength=256), torch.bincount(vb.long(), minlength=256))
+        assert not torch.equal(va, vb) or va.numel() <= 16
+    dp = dict(d, w1=w1p, w2=w2p)
+    got, _, _, _ = U.run_forward(wl, dp, p=pp)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+
+
+@pytest.mark.parametrize("name", ["mixtral_bf16", "dsv3_bf16", "decode_fp8_m64", "decode_fp8_m256"])
+def test_packed_weights_full_size(name):
+    """The configuration the benchmark times (packed weights, full size):
+    bitwise equal to the row-major run and within the bar of the oracle."""
+    wl = WORKLOADS[name]
+    d = make_inputs(wl, seed=0, device="cuda")
+    ref, sref, _, _ = U.run_forward(wl, d)
+    pp = U.problem(wl, weight_layout=moe.WEIGHTS_PACKED)
+    w1p, w2p = moe.pack_weights(pp, d["w1"], d["w2"])
+    got, sgot, _, _ = U.run_forward(wl, dict(d, w1=w1p, w2=w2p), p=pp)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    del w1p, w2p
+    toks = sample_tokens(wl.M, 6, seed=3)
+    oref, _, _ = oracle.moe_tokens(wl, d, toks)
+    err = U.rel_err(got.float().cpu().numpy()[toks], oref)
+    print(f"  {name} packed: max rel err {err:.3e}", flush=True)
+    assert err <= U.tol_for(wl)
