@@ -26,7 +26,8 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 DTYPE_NAME = {0: "f32", 1: "bf16", 2: "fp8"}
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
-GEMM_SOURCE = os.path.join(ROOT, "combine_topk_softmax_amd", "csrc", "grouped_gemm.hip")
+GEMM_SOURCES = [os.path.join(ROOT, "combine_topk_softmax_amd", "csrc", f)
+                for f in ("stream_gemm.hip", "grouped_gemm.hip", "moe_device.h")]
 
 
 def parse():
@@ -39,14 +40,19 @@ def parse():
                     help="tokens of the CPU-oracle sample (0: sized to ~15 s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="also time hipGraph replay of the step")
+    ap.add_argument("--weights", choices=["packed", "row_major"], default="packed",
+                    help="expert weight layout (packed once before timing, as at model load)")
     ap.add_argument("--copy-calibration", type=float, default=0.0,
                     help="only run a plain device copy of this many GiB (counter calibration)")
     return ap.parse_args()
 
 
 def kernel_source_hash() -> str:
-    with open(GEMM_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in GEMM_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def gemm1_algorithmic(wl, counts):
@@ -132,9 +138,20 @@ def main():
     torch.cuda.set_device(0)
     print(f"[bench] generating inputs for {wl.name}", file=sys.stderr, flush=True)
     d = make_inputs(wl, seed=0, device="cuda")
+    packed = args.weights == "packed" and wl.I % 128 == 0
     p = moe.make_problem(wl.E, wl.M, 2 * wl.I, wl.K, wl.topk, format=wl.format, act_dtype=wl.act_dtype,
                          w_dtype=wl.w_dtype, act_quant=wl.act_quant, scoring=wl.scoring,
-                         renormalize=wl.renormalize, max_tokens_per_expert=wl.capacity, shared_N=2 * wl.shared_I)
+                         renormalize=wl.renormalize, max_tokens_per_expert=wl.capacity, shared_N=2 * wl.shared_I,
+                         weight_layout=moe.WEIGHTS_PACKED if packed else moe.WEIGHTS_ROW_MAJOR)
+    pack_ms = None
+    gw = {"w1": d["w1"], "w2": d["w2"]}
+    if packed:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        gw["w1"], gw["w2"] = moe.pack_weights(p, d["w1"], d["w2"])
+        b.record()
+        torch.cuda.synchronize()
+        pack_ms = a.elapsed_time(b)
     ws = moe.empty_workspace(p)
     L = moe.workspace_layout(p)
     odt = torch.float32 if wl.act_dtype == 0 else torch.bfloat16
@@ -146,7 +163,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(events=None):
-        moe.moe_forward(p, d["logits"], d["x"], d["w1"], d.get("w1_scale"), d["w2"], d.get("w2_scale"), out, ws,
+        moe.moe_forward(p, d["logits"], d["x"], gw["w1"], d.get("w1_scale"), gw["w2"], d.get("w2_scale"), out, ws,
                         stream=stream, shared=shared, shared_streams=streams, events=events)
 
     for _ in range(args.warmup):
@@ -171,6 +188,7 @@ def main():
     gemm1_ms = float(stage_avg[2])
 
     counts = ws[L.counts: L.counts + 4 * wl.E].view(torch.int32).cpu().numpy()
+    streaming = wl.w_dtype != 0 and wl.M * wl.topk <= wl.E * (128 if wl.w_dtype == 2 else 256)
     g1_bytes, g1_flops = gemm1_algorithmic(wl, counts)
     achieved = g1_bytes / (gemm1_ms * 1e-3) / 1e9
     traffic = measured_traffic(wl.name)
@@ -183,7 +201,7 @@ def main():
         s.wait_stream(stream)
         with torch.cuda.stream(s):
             with torch.cuda.graph(g, stream=s):
-                moe.moe_forward(p, d["logits"], d["x"], d["w1"], d.get("w1_scale"), d["w2"], d.get("w2_scale"),
+                moe.moe_forward(p, d["logits"], d["x"], gw["w1"], d.get("w1_scale"), gw["w2"], d.get("w2_scale"),
                                 out, ws, shared=shared, shared_streams=streams)
         torch.cuda.synchronize()
         for _ in range(args.warmup):
@@ -218,10 +236,12 @@ def main():
         "data": "synthetic (seeded; x ~ N(0,1), weights ~ N(0,0.02), logits per workload recipe)",
         "config": {"workload": wl.name, "tokens": wl.M, "hidden": wl.K, "intermediate": wl.I, "experts": wl.E,
                    "topk": wl.topk, "format": "batched_experts" if wl.format else "standard",
-                   "shared_expert_intermediate": wl.shared_I or None},
+                   "shared_expert_intermediate": wl.shared_I or None,
+                   "weight_layout": "packed (one-time reorder before timing)" if packed else "row_major"},
+        "weight_pack_ms": pack_ms,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "grouped_gemm_kernel (gated: w1 + SiLU-and-mul)",
+                     "kernel": "gated grouped GEMM (w1 + SiLU-and-mul), " + ("weight streaming" if streaming else "MFMA tiles"),
                      "algorithmic_bytes_per_launch": g1_bytes, "avg_launch_ms": gemm1_ms},
         "gemm_tflops": {"gated_gemm": g1_flops / (gemm1_ms * 1e-3) / 1e12,
                         "both_gemms": wl.gemm_flops() / ((stage_avg[2] + stage_avg[3]) * 1e-3) / 1e12,
