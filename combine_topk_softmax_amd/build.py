@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_gfx950.so")
-SOURCES = ["moe_api.hip", "route.hip", "dispatch.hip", "grouped_gemm.hip", "stream_gemm.hip", "combine.hip", "pack.hip"]
+SOURCES = ["moe_api.hip", "route.hip", "dispatch.hip", "grouped_gemm.hip", "stream_gemm.hip", "mfma_gemm.hip", "combine.hip", "pack.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

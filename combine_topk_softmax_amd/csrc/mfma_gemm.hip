@@ -1,0 +1,239 @@
+// Compute-bound grouped expert GEMMs (bf16) for prefill batches whose experts
+// hold many rows: the same two products as grouped_gemm.hip (modular_kernel.py
+// page, FusedMoEPermuteExpertsUnpermute: "matmul + act_mul + optionally quant
+// + matmul"; per-expert row counts read on the device, as on the worst-tokens
+// page),
+//
+//   gated GEMM   act[slot, j] = silu(A w1[e, j]) * (A w1[e, I + j])
+//   down GEMM    out[row(slot), :] = act[slot, :] w2[e]^T
+//
+// laid out for gfx950's matrix cores when flops, not weight bytes, set the
+// time:
+//
+//  * a workgroup computes a 256-row x 256-column tile (rows: one expert's
+//    slots from the device tile plan; columns: 128 gate + the matching 128 up
+//    weight rows, or 256 output columns), so every operand byte staged in LDS
+//    feeds 256 MFMA columns or rows;
+//  * 8 wavefronts in a 2 x 4 grid, each owning 128 x 64 as 4 x 2 blocks of
+//    v_mfma_f32_32x32x16_bf16 (128 fp32 accumulators per lane, two
+//    wavefronts per SIMD);
+//  * K advances 64 elements per step; both operands go global -> registers ->
+//    a double-buffered, XOR-swizzled LDS tile (64 KB per stage), the next
+//    step's global loads being in flight during the current step's 32 MFMAs
+//    per wavefront; one barrier per step;
+//  * all loads are unconditional (rows past the count read a valid row and are
+//    zeroed on the way into LDS), so the compiler never waits for every
+//    outstanding load in front of the MFMAs;
+//  * work items are dealt out XCD by XCD and, inside an XCD's range, grouped
+//    four row tiles at a time per column tile, so the workgroups resident on
+//    one XCD share both activation rows and weight panels through its L2.
+#include "moe_device.h"
+
+namespace moe {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 512;
+constexpr int kRows = 256;            // tile rows (slots)
+constexpr int kCols = 256;            // tile columns (weight rows)
+constexpr int kStep = 128;            // bytes of K per step (64 bf16)
+constexpr int kGroupM = 4;            // row tiles per L2 group
+
+// Swizzled byte address inside a [rows][128 B] LDS tile: the 16-byte chunk
+// index is XORed with (row / 2) % 8, so the 16 lanes of one 128-bit access
+// pass (16 consecutive rows, one logical chunk) hit 16 distinct 4-bank groups
+// of gfx950's 64 banks.
+__device__ __forceinline__ int swz(int row, int b) {
+  return row * kStep + ((((b >> 4) ^ ((row >> 1) & 7)) << 4) | (b & 15));
+}
+
+template <bool GATED, bool PACKED>
+__global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const GemmParams g, int n_tiles) {
+  __shared__ __attribute__((aligned(16))) uint8_t As[2][kRows * kStep];
+  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][kCols * kStep];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wm = wv >> 2, wn = wv & 3;
+  const bool dense = g.t.dense_rows > 0;
+  const int m_tiles = dense ? (g.t.dense_rows + kRows - 1) / kRows : *g.t.tile_count;
+  const int total = m_tiles * n_tiles;
+
+  // XCD-contiguous item ranges, then row-tile groups inside each range.
+  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+  const int per = (total + 7) >> 3;
+  const int item = xcd * per + local;
+  if (local >= per || item >= total) return;
+  const int grp = item / (kGroupM * n_tiles);
+  const int gm = min(kGroupM, m_tiles - grp * kGroupM);
+  const int within = item - grp * kGroupM * n_tiles;
+  const int mt = grp * kGroupM + within % gm;
+  const int nt = within / gm;
+
+  int e, T;
+  int64_t row0;
+  if (dense) {
+    e = 0;
+    row0 = (int64_t)mt * kRows;
+    T = min(kRows, g.t.dense_rows - mt * kRows);
+  } else {
+    const int32_t *d = g.t.tiles + (int64_t)mt * 4;
+    e = d[0];
+    row0 = (int64_t)d[1] + d[2];
+    T = d[3];
+  }
+
+  const int64_t row_bytes = g.Kred * 2;
+  const int nk = (int)(row_bytes / kStep);
+  const int chunk = tid & 7;
+  const PackedGeom pg = packed_geom(g.Nw, row_bytes, GATED);
+  const int64_t kstride = PACKED ? packed_kstep_stride(pg) : kStep;
+
+  // This thread stages chunk `chunk` of rows (tid / 8) + 64 i, i < 4, of both
+  // operand tiles.
+  const uint8_t *a_src[4];
+  bool a_ok[4];
+  const uint8_t *b_src[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (tid >> 3) + 64 * i;
+    a_src[i] = reinterpret_cast<const uint8_t *>(g.a) + chunk * 16;
+    a_ok[i] = false;
+    if (r < T) {
+      const int64_t s = row0 + r;
+      int64_t arow = s;
+      if (g.perm) {
+        const int f = g.perm[s];
+        arow = (f >= 0 && f < g.n_pairs) ? f / g.topk : -1;
+      }
+      if (arow >= 0) {
+        a_src[i] = reinterpret_cast<const uint8_t *>(g.a) + arow * row_bytes + chunk * 16;
+        a_ok[i] = true;
+      }
+    }
+    int64_t wrow;
+    if (GATED)
+      wrow = r < 128 ? (int64_t)nt * 128 + r : g.half_n + (int64_t)nt * 128 + (r - 128);
+    else
+      wrow = (int64_t)nt * kCols + r;
+    if (PACKED)
+      b_src[i] = reinterpret_cast<const uint8_t *>(g.w) + packed_piece(pg, e, wrow, 0, chunk);
+    else
+      b_src[i] = reinterpret_cast<const uint8_t *>(g.w) + ((int64_t)e * g.Nw + wrow) * row_bytes + chunk * 16;
+  }
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.0f;
+
+  uint4 ra[4], rb[4];
+  auto gload = [&](int ks) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ra[i] = *reinterpret_cast<const uint4 *>(a_src[i] + (int64_t)ks * kStep);
+      rb[i] = *reinterpret_cast<const uint4 *>(b_src[i] + (int64_t)ks * kstride);
+    }
+  };
+  auto lstore = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = (tid >> 3) + 64 * i;
+      *reinterpret_cast<uint4 *>(&As[st][swz(r, chunk * 16)]) = a_ok[i] ? ra[i] : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4 *>(&Bs[st][swz(r, chunk * 16)]) = rb[i];
+    }
+  };
+  // B rows of this wavefront's two column blocks: gate and up (gated), or two
+  // adjacent 32-column blocks (down).
+  const int brow0 = GATED ? wn * 32 : wn * 64;
+  const int brow1 = GATED ? 128 + wn * 32 : wn * 64 + 32;
+  auto compute = [&](int st) {
+    const uint8_t *A = As[st];
+    const uint8_t *B = Bs[st];
+#pragma unroll
+    for (int kk = 0; kk < kStep / 32; ++kk) {
+      const int boff = kk * 32 + (lane >> 5) * 16;
+      const bf16x8 b0 = *reinterpret_cast<const bf16x8 *>(B + swz(brow0 + (lane & 31), boff));
+      const bf16x8 b1 = *reinterpret_cast<const bf16x8 *>(B + swz(brow1 + (lane & 31), boff));
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(A + swz(wm * 128 + mb * 32 + (lane & 31), boff));
+        acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc[mb][0], 0, 0, 0);
+        acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc[mb][1], 0, 0, 0);
+      }
+    }
+  };
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  gload(min(1, nk - 1));
+  // The step after the last reloads the last one instead of branching around
+  // the loads.
+  for (int ks = 0; ks < nk; ++ks) {
+    compute(ks & 1);
+    lstore((ks + 1) & 1);
+    gload(min(ks + 2, nk - 1));
+    __syncthreads();
+  }
+
+  // Epilogue.  Accumulator element i of a 32x32 block sits at column
+  // (lane % 32) and row 8 (i / 4) + 4 (lane / 32) + i % 4.
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = wm * 128 + mb * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+      if (r >= T) continue;
+      const int64_t slot = row0 + r;
+      if constexpr (GATED) {
+        const float gt = acc[mb][0][i], up = acc[mb][1][i];
+        const float v = gt / (1.0f + expf(-gt)) * up;
+        const int64_t col = (int64_t)nt * 128 + wn * 32 + (lane & 31);
+        reinterpret_cast<uint16_t *>(g.out)[slot * g.ldo + col] = f32_to_bf16_bits(v);
+      } else {
+        const int64_t orow = g.out_perm ? g.out_perm[slot] : slot;
+        if (orow < 0 || (g.out_perm && orow >= g.n_pairs)) continue;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const int64_t col = (int64_t)nt * kCols + wn * 64 + nb * 32 + (lane & 31);
+          reinterpret_cast<uint16_t *>(g.out)[orow * g.ldo + col] = f32_to_bf16_bits(acc[mb][nb][i]);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+int mfma_gemm_tile_rows() { return kRows; }
+
+bool mfma_gemm_fits(int w_dtype, int act_dtype, int64_t K, int64_t I) {
+  // bf16 in and out; gated column tiles of 128 act columns, down column tiles
+  // of 256 outputs, K-steps of 64 elements on both reductions.
+  return w_dtype == MOE_DTYPE_BF16 && act_dtype == MOE_DTYPE_BF16 && I % 128 == 0 && K % 256 == 0 &&
+         I % 64 == 0;
+}
+
+int mfma_gemm_n_tiles(GemmKind kind, int64_t Nw) { return (int)(kind == kGemmGatedAct ? Nw / 256 : Nw / kCols); }
+
+hipError_t launch_mfma_gemm(GemmKind kind, const GemmParams &g, int n_tiles, hipStream_t s) {
+  const int m_tiles = g.t.dense_rows > 0 ? (g.t.dense_rows + kRows - 1) / kRows : g.t.max_tiles;
+  // whole rounds of 8 blocks: every XCD needs as many blocks as the longest
+  // XCD range of items
+  const dim3 grid((unsigned)(((m_tiles * n_tiles + 7) / 8) * 8)), block(kThreads);
+  const bool gated = kind == kGemmGatedAct;
+  if (gated)
+    g.w_packed ? mfma_gemm_kernel<true, true><<<grid, block, 0, s>>>(g, n_tiles)
+               : mfma_gemm_kernel<true, false><<<grid, block, 0, s>>>(g, n_tiles);
+  else
+    g.w_packed ? mfma_gemm_kernel<false, true><<<grid, block, 0, s>>>(g, n_tiles)
+               : mfma_gemm_kernel<false, false><<<grid, block, 0, s>>>(g, n_tiles);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -164,7 +164,10 @@ moe_status do_experts(const moe_problem &p, const void *a, const float *a_scale,
   // streaming tile (weights then dominate the bytes); MFMA tiles otherwise.
   const bool streaming = p.w_dtype != MOE_DTYPE_F32 && stream_gemm_fits(p.w_dtype, p.K, I) &&
                          p.M * p.topk <= p.E * (int64_t)stream_gemm_tile_rows(p.w_dtype);
-  const int tile_rows = streaming ? stream_gemm_tile_rows(p.w_dtype) : (int)L.tile_rows;
+  // Past that point the GEMMs are bound by the matrix cores: 256 x 256 tiles
+  // where the shapes allow, the general 128 x 128 kernel otherwise.
+  const bool big = !streaming && mfma_gemm_fits(p.w_dtype, p.act_dtype, p.K, I);
+  const int tile_rows = streaming ? stream_gemm_tile_rows(p.w_dtype) : big ? mfma_gemm_tile_rows() : (int)L.tile_rows;
   MOE_HIP(launch_plan_tiles(p, counts, at<int32_t>(ws, L.offsets), L.perm_len, tile_rows,
                             (int)L.max_tiles, tiles, status, s));
   record(ev, 2, s);
@@ -193,6 +196,8 @@ moe_status do_experts(const moe_problem &p, const void *a, const float *a_scale,
   if (streaming)
     MOE_HIP(launch_stream_gemm(p.w_dtype, fp8 ? MOE_DTYPE_F32 : p.act_dtype, kGemmGatedAct, g1,
                                (int)(I / 128), s));
+  else if (big)
+    MOE_HIP(launch_mfma_gemm(kGemmGatedAct, g1, mfma_gemm_n_tiles(kGemmGatedAct, g1.Nw), s));
   else
     MOE_HIP(launch_grouped_gemm(p.w_dtype, fp8 ? MOE_DTYPE_F32 : p.act_dtype, kGemmGatedAct, g1,
                                 (int)(I / 64), s));
@@ -220,6 +225,8 @@ moe_status do_experts(const moe_problem &p, const void *a, const float *a_scale,
   g2.t = gt;
   if (streaming)
     MOE_HIP(launch_stream_gemm(p.w_dtype, p.act_dtype, kGemmDown, g2, (int)(p.K / 128), s));
+  else if (big)
+    MOE_HIP(launch_mfma_gemm(kGemmDown, g2, mfma_gemm_n_tiles(kGemmDown, g2.Nw), s));
   else
     MOE_HIP(launch_grouped_gemm(p.w_dtype, p.act_dtype, kGemmDown, g2, (int)(p.K / 128), s));
   record(ev, 4, s);
@@ -246,7 +253,11 @@ moe_status do_shared(const moe_problem &p, const void *x, const void *w1, const 
   g1.ldo = Is;
   g1.half_n = Is;
   g1.t = gt;
-  MOE_HIP(launch_grouped_gemm(p.act_dtype, p.act_dtype, kGemmGatedAct, g1, (int)(Is / 64), s));
+  const bool big = mfma_gemm_fits(p.act_dtype, p.act_dtype, p.K, Is);
+  if (big)
+    MOE_HIP(launch_mfma_gemm(kGemmGatedAct, g1, mfma_gemm_n_tiles(kGemmGatedAct, g1.Nw), s));
+  else
+    MOE_HIP(launch_grouped_gemm(p.act_dtype, p.act_dtype, kGemmGatedAct, g1, (int)(Is / 64), s));
   GemmParams g2;
   memset(&g2, 0, sizeof(g2));
   g2.a = at<void>(ws, L.shared_act);
@@ -258,7 +269,10 @@ moe_status do_shared(const moe_problem &p, const void *x, const void *w1, const 
   g2.out = out;
   g2.ldo = p.K;
   g2.t = gt;
-  MOE_HIP(launch_grouped_gemm(p.act_dtype, p.act_dtype, kGemmDown, g2, (int)(p.K / 128), s));
+  if (big)
+    MOE_HIP(launch_mfma_gemm(kGemmDown, g2, mfma_gemm_n_tiles(kGemmDown, g2.Nw), s));
+  else
+    MOE_HIP(launch_grouped_gemm(p.act_dtype, p.act_dtype, kGemmDown, g2, (int)(p.K / 128), s));
   return MOE_OK;
 }
 

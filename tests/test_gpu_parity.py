@@ -164,6 +164,16 @@ SMALL = {
     "fp8_batched": WORKLOADS["decode_fp8_m64"].replace(M=90, K=384, I=256, E=5, topk=2, capacity=90),
     "fp8_standard": WORKLOADS["decode_fp8_m64"].replace(M=90, K=256, I=256, E=6, topk=3,
                                                         format=FORMAT_STANDARD, capacity=0),
+    # more rows per expert than one weight-streaming tile: 256 x 256 MFMA tiles,
+    # several row tiles per expert plus a ragged last one, 2 column tiles
+    "bf16_mfma": WORKLOADS["mixtral_bf16"].replace(M=700, K=512, I=256, E=4, topk=2, renormalize=False,
+                                                   logits_dist="normal"),
+    "bf16_mfma_batched": WORKLOADS["mixtral_bf16"].replace(M=600, K=256, I=128, E=3, topk=2,
+                                                           format=FORMAT_BATCHED, capacity=600,
+                                                           logits_dist="normal"),
+    # the same regime with I % 128 != 0: the general 128 x 128 tile kernel
+    "bf16_tiled_I192": WORKLOADS["mixtral_bf16"].replace(M=700, K=384, I=192, E=4, topk=2, renormalize=False,
+                                                         logits_dist="normal"),
 }
 
 
@@ -208,6 +218,27 @@ def test_experts_parity_every_pair(name):
     assert np.all(np.isfinite(mine))
     err = U.rel_err(mine, ref)
     print(f"  {name}: max rel err {err:.3e}", flush=True)
+    assert err <= U.tol_for(wl)
+
+
+@pytest.mark.parametrize("M,K,Is", [(300, 512, 256), (64, 256, 128), (513, 768, 384)])
+def test_shared_expert_parity(M, K, Is):
+    """The always-on shared expert alone (dense gated MLP over all M tokens),
+    with M not a multiple of the row tile."""
+    wl = WORKLOADS["dsv3_bf16"].replace(M=M, K=K, I=128, E=4, topk=2, shared_I=Is)
+    d = make_inputs(wl, seed=16, device="cpu")
+    p = U.problem(wl)
+    ws = moe.empty_workspace(p)
+    g = U.to_cuda(d)
+    out = torch.full((M, K), float("nan"), dtype=torch.bfloat16, device="cuda")
+    moe.moe_shared_expert(p, g["x"], g["w1s"], g["w2s"], out, ws)
+    torch.cuda.synchronize()
+    toks = list(range(M))
+    ref = oracle.dense_mlp_tokens(d["x"], d["w1s"], d["w2s"], Is, wl.act_dtype, toks)
+    got = out.float().cpu().numpy()
+    assert np.all(np.isfinite(got))
+    err = U.rel_err(got, ref)
+    print(f"  shared M={M} K={K} Is={Is}: max rel err {err:.3e}", flush=True)
     assert err <= U.tol_for(wl)
 
 
