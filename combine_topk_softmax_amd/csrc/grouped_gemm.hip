@@ -34,6 +34,9 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+// Staging registers are native vectors: HIP's uint4 is a struct whose copies
+// become memcpy, which keeps a staging array in memory (LDS or scratch).
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // One MFMA flavour per element size.  A step consumes kLaneBytes per lane of
 // each operand: lane l holds row (l % 32), k-half (l / 32).
@@ -188,14 +191,14 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmParams g) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.0f;
 
-  uint4 ra[4], rb[4];
+  u32x4 ra[4], rb[4];
   float sa_reg = 0.0f;
   auto gload = [&](int ks) {
     const int64_t off = (int64_t)ks * kRowBytes;   // activation bytes
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ra[i] = *reinterpret_cast<const uint4 *>(a_src[i] + off);
-      rb[i] = *reinterpret_cast<const uint4 *>(b_src[i] + (int64_t)ks * kstride);
+      ra[i] = *reinterpret_cast<const u32x4 *>(a_src[i] + off);
+      rb[i] = *reinterpret_cast<const u32x4 *>(b_src[i] + (int64_t)ks * kstride);
     }
     if constexpr (kScaled) sa_reg = sa_src[ks];
   };
@@ -203,8 +206,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(const GemmParams g) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = (tid >> 3) + 32 * i;
-      *reinterpret_cast<uint4 *>(&lds[st][0][swz(r, chunk * 16)]) = a_ok[i] ? ra[i] : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4 *>(&lds[st][1][swz(r, chunk * 16)]) = rb[i];
+      *reinterpret_cast<u32x4 *>(&lds[st][0][swz(r, chunk * 16)]) = a_ok[i] ? ra[i] : u32x4{0, 0, 0, 0};
+      *reinterpret_cast<u32x4 *>(&lds[st][1][swz(r, chunk * 16)]) = rb[i];
     }
     if constexpr (kScaled)
       if (tid < 128) lds_sa[st][tid] = sa_ok ? sa_reg : 0.0f;

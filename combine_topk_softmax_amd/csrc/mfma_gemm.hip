@@ -25,7 +25,7 @@
 //    zeroed on the way into LDS), so the compiler never waits for every
 //    outstanding load in front of the MFMAs;
 //  * work items are dealt out XCD by XCD and, inside an XCD's range, grouped
-//    four row tiles at a time per column tile, so the workgroups resident on
+//    eight row tiles at a time per column tile, so the workgroups resident on
 //    one XCD share both activation rows and weight panels through its L2.
 #include "moe_device.h"
 
@@ -34,12 +34,18 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+// Staging registers are native vectors: HIP's uint4 is a struct whose copies
+// become memcpy, which keeps a staging array in memory (LDS or scratch).
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 512;
 constexpr int kRows = 256;            // tile rows (slots)
 constexpr int kCols = 256;            // tile columns (weight rows)
 constexpr int kStep = 128;            // bytes of K per step (64 bf16)
-constexpr int kGroupM = 4;            // row tiles per L2 group
+#ifndef MOE_MFMA_GROUP_M
+#define MOE_MFMA_GROUP_M 8
+#endif
+constexpr int kGroupM = MOE_MFMA_GROUP_M;   // row tiles per L2 group
 
 // Swizzled byte address inside a [rows][128 B] LDS tile: the 16-byte chunk
 // index is XORed with (row / 2) % 8, so the 16 lanes of one 128-bit access
@@ -131,20 +137,20 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const GemmParams g,
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.0f;
 
-  uint4 ra[4], rb[4];
+  u32x4 ra[4], rb[4];
   auto gload = [&](int ks) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ra[i] = *reinterpret_cast<const uint4 *>(a_src[i] + (int64_t)ks * kStep);
-      rb[i] = *reinterpret_cast<const uint4 *>(b_src[i] + (int64_t)ks * kstride);
+      ra[i] = *reinterpret_cast<const u32x4 *>(a_src[i] + (int64_t)ks * kStep);
+      rb[i] = *reinterpret_cast<const u32x4 *>(b_src[i] + (int64_t)ks * kstride);
     }
   };
   auto lstore = [&](int st) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = (tid >> 3) + 64 * i;
-      *reinterpret_cast<uint4 *>(&As[st][swz(r, chunk * 16)]) = a_ok[i] ? ra[i] : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4 *>(&Bs[st][swz(r, chunk * 16)]) = rb[i];
+      *reinterpret_cast<u32x4 *>(&As[st][swz(r, chunk * 16)]) = a_ok[i] ? ra[i] : u32x4{0, 0, 0, 0};
+      *reinterpret_cast<u32x4 *>(&Bs[st][swz(r, chunk * 16)]) = rb[i];
     }
   };
   // B rows of this wavefront's two column blocks: gate and up (gated), or two
