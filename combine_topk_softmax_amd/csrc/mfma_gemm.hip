@@ -18,11 +18,11 @@
 //    v_mfma_f32_32x32x16_bf16 (128 fp32 accumulators per lane, two
 //    wavefronts per SIMD);
 //  * K advances 64 elements per step; both operands go global -> registers ->
-//    a double-buffered, XOR-swizzled LDS tile (64 KB per stage), the next
+//    a double-buffered, padded LDS tile (72 KB per stage), the next
 //    step's global loads being in flight during the current step's 32 MFMAs
 //    per wavefront; one barrier per step;
-//  * all loads are unconditional (rows past the count read a valid row and are
-//    zeroed on the way into LDS), so the compiler never waits for every
+//  * all loads are unconditional (rows past the count read a valid row whose
+//    products are never stored), so the compiler never waits for every
 //    outstanding load in front of the MFMAs;
 //  * work items are dealt out XCD by XCD and, inside an XCD's range, grouped
 //    eight row tiles at a time per column tile, so the workgroups resident on
@@ -47,18 +47,19 @@ constexpr int kStep = 128;            // bytes of K per step (64 bf16)
 #endif
 constexpr int kGroupM = MOE_MFMA_GROUP_M;   // row tiles per L2 group
 
-// Swizzled byte address inside a [rows][128 B] LDS tile: the 16-byte chunk
-// index is XORed with (row / 2) % 8, so the 16 lanes of one 128-bit access
-// pass (16 consecutive rows, one logical chunk) hit 16 distinct 4-bank groups
-// of gfx950's 64 banks.
-__device__ __forceinline__ int swz(int row, int b) {
-  return row * kStep + ((((b >> 4) ^ ((row >> 1) & 7)) << 4) | (b & 15));
-}
+// LDS tiles are [rows][144 B]: 128 bytes of K plus 16 bytes of padding.  A
+// fragment read is one 16-byte chunk of 16 consecutive rows per 128-bit access
+// pass; with a 144-byte pitch those rows start 36 banks apart, which covers
+// gfx950's 64 banks exactly once.  Unlike an XOR swizzle, the padding keeps
+// every K sub-step at a constant offset from the row's address, so a fragment
+// needs one address register per row block instead of one per sub-step.
+constexpr int kPitch = kStep + 16;
+__device__ __forceinline__ int lds_at(int row, int b) { return row * kPitch + b; }
 
 template <bool GATED, bool PACKED>
 __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const GemmParams g, int n_tiles) {
-  __shared__ __attribute__((aligned(16))) uint8_t As[2][kRows * kStep];
-  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][kCols * kStep];
+  __shared__ __attribute__((aligned(16))) uint8_t As[2][kRows * kPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][kCols * kPitch];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = wv >> 2, wn = wv & 3;
@@ -97,15 +98,34 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const GemmParams g,
   const int64_t kstride = PACKED ? packed_kstep_stride(pg) : kStep;
 
   // This thread stages chunk `chunk` of rows (tid / 8) + 64 i, i < 4, of both
-  // operand tiles.
+  // operand tiles.  Rows past the tile's count and padding slots read row 0
+  // instead: an A row only feeds its own output row, and the epilogue writes
+  // nothing for those rows, so their contents never matter (and no select on
+  // loaded data forces an early wait for the loads).
   const uint8_t *a_src[4];
-  bool a_ok[4];
-  const uint8_t *b_src[4];
+  // Weight rows: base_i + (tid / 8) with base_i a multiple of 64, so in both
+  // layouts the address splits into a per-lane part (row within the 64-row
+  // group, chunk) shared by all four rows and a wavefront-uniform part per row
+  // group, which stays in scalar registers.
+  int64_t b_uni[4];
+  auto wbase = [&](int i) -> int64_t {
+    if (GATED) return i < 2 ? (int64_t)nt * 128 + 64 * i : g.half_n + (int64_t)nt * 128 + 64 * (i - 2);
+    return (int64_t)nt * kCols + 64 * i;
+  };
+  const int r0 = tid >> 3;
+  int64_t b_lane;
+  if (PACKED)
+    b_lane = packed_piece(pg, e, wbase(0) + r0, 0, chunk) - packed_piece(pg, e, wbase(0), 0, 0);
+  else
+    b_lane = (int64_t)r0 * row_bytes + chunk * 16;
+  const uint8_t *b_src = reinterpret_cast<const uint8_t *>(g.w) + b_lane;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    b_uni[i] = PACKED ? packed_piece(pg, e, wbase(i), 0, 0) : ((int64_t)e * g.Nw + wbase(i)) * row_bytes;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = (tid >> 3) + 64 * i;
     a_src[i] = reinterpret_cast<const uint8_t *>(g.a) + chunk * 16;
-    a_ok[i] = false;
     if (r < T) {
       const int64_t s = row0 + r;
       int64_t arow = s;
@@ -113,20 +133,8 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const GemmParams g,
         const int f = g.perm[s];
         arow = (f >= 0 && f < g.n_pairs) ? f / g.topk : -1;
       }
-      if (arow >= 0) {
-        a_src[i] = reinterpret_cast<const uint8_t *>(g.a) + arow * row_bytes + chunk * 16;
-        a_ok[i] = true;
-      }
+      if (arow >= 0) a_src[i] = reinterpret_cast<const uint8_t *>(g.a) + arow * row_bytes + chunk * 16;
     }
-    int64_t wrow;
-    if (GATED)
-      wrow = r < 128 ? (int64_t)nt * 128 + r : g.half_n + (int64_t)nt * 128 + (r - 128);
-    else
-      wrow = (int64_t)nt * kCols + r;
-    if (PACKED)
-      b_src[i] = reinterpret_cast<const uint8_t *>(g.w) + packed_piece(pg, e, wrow, 0, chunk);
-    else
-      b_src[i] = reinterpret_cast<const uint8_t *>(g.w) + ((int64_t)e * g.Nw + wrow) * row_bytes + chunk * 16;
   }
 
   f32x16 acc[4][2];
@@ -137,20 +145,22 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const GemmParams g,
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.0f;
 
-  u32x4 ra[4], rb[4];
-  auto gload = [&](int ks) {
+  // Two register sets of staged operands: step j's loads land in set j % 2,
+  // issued two steps before they are stored to LDS.
+  u32x4 ra[2][4], rb[2][4];
+  auto gload = [&](int set, int ks) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ra[i] = *reinterpret_cast<const u32x4 *>(a_src[i] + (int64_t)ks * kStep);
-      rb[i] = *reinterpret_cast<const u32x4 *>(b_src[i] + (int64_t)ks * kstride);
+      ra[set][i] = *reinterpret_cast<const u32x4 *>(a_src[i] + (int64_t)ks * kStep);
+      rb[set][i] = *reinterpret_cast<const u32x4 *>(b_src + b_uni[i] + (int64_t)ks * kstride);
     }
   };
-  auto lstore = [&](int st) {
+  auto lstore = [&](int st, int set) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = (tid >> 3) + 64 * i;
-      *reinterpret_cast<u32x4 *>(&As[st][swz(r, chunk * 16)]) = a_ok[i] ? ra[i] : u32x4{0, 0, 0, 0};
-      *reinterpret_cast<u32x4 *>(&Bs[st][swz(r, chunk * 16)]) = rb[i];
+      *reinterpret_cast<u32x4 *>(&As[st][lds_at(r, chunk * 16)]) = ra[set][i];
+      *reinterpret_cast<u32x4 *>(&Bs[st][lds_at(r, chunk * 16)]) = rb[set][i];
     }
   };
   // B rows of this wavefront's two column blocks: gate and up (gated), or two
@@ -163,27 +173,36 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const GemmParams g,
 #pragma unroll
     for (int kk = 0; kk < kStep / 32; ++kk) {
       const int boff = kk * 32 + (lane >> 5) * 16;
-      const bf16x8 b0 = *reinterpret_cast<const bf16x8 *>(B + swz(brow0 + (lane & 31), boff));
-      const bf16x8 b1 = *reinterpret_cast<const bf16x8 *>(B + swz(brow1 + (lane & 31), boff));
+      const bf16x8 b0 = *reinterpret_cast<const bf16x8 *>(B + lds_at(brow0 + (lane & 31), boff));
+      const bf16x8 b1 = *reinterpret_cast<const bf16x8 *>(B + lds_at(brow1 + (lane & 31), boff));
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(A + swz(wm * 128 + mb * 32 + (lane & 31), boff));
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(A + lds_at(wm * 128 + mb * 32 + (lane & 31), boff));
         acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc[mb][0], 0, 0, 0);
         acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc[mb][1], 0, 0, 0);
       }
     }
   };
 
-  gload(0);
-  lstore(0);
+  // Pipeline: LDS holds steps ks (being multiplied) and ks + 1 (stored at the
+  // end of step ks), registers hold steps ks + 1 and ks + 2 in flight, so every
+  // load has two steps of matrix work to arrive in.  Steps past the last
+  // reload the last one instead of branching around the loads.  nk is even
+  // (the host requires K and I to be multiples of 128 elements), so the loop
+  // runs in pairs and every register-set index is a constant.
+  gload(0, 0);
+  lstore(0, 0);
   __syncthreads();
-  gload(min(1, nk - 1));
-  // The step after the last reloads the last one instead of branching around
-  // the loads.
-  for (int ks = 0; ks < nk; ++ks) {
-    compute(ks & 1);
-    lstore((ks + 1) & 1);
-    gload(min(ks + 2, nk - 1));
+  gload(1, min(1, nk - 1));
+  gload(0, min(2, nk - 1));
+  for (int ks = 0; ks < nk; ks += 2) {
+    compute(0);
+    lstore(1, 1);
+    gload(1, min(ks + 3, nk - 1));
+    __syncthreads();
+    compute(1);
+    lstore(0, 0);
+    gload(0, min(ks + 4, nk - 1));
     __syncthreads();
   }
 

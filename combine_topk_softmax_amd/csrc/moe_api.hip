@@ -195,7 +195,7 @@ moe_status do_experts(const moe_problem &p, const void *a, const float *a_scale,
   g1.t = gt;
   if (streaming)
     MOE_HIP(launch_stream_gemm(p.w_dtype, fp8 ? MOE_DTYPE_F32 : p.act_dtype, kGemmGatedAct, g1,
-                               (int)(I / 128), s));
+                               (int)(I / 128), 1, s));
   else if (big)
     MOE_HIP(launch_mfma_gemm(kGemmGatedAct, g1, mfma_gemm_n_tiles(kGemmGatedAct, g1.Nw), s));
   else
@@ -224,7 +224,8 @@ moe_status do_experts(const moe_problem &p, const void *a, const float *a_scale,
   g2.w_packed = p.weight_layout == MOE_WEIGHTS_PACKED;
   g2.t = gt;
   if (streaming)
-    MOE_HIP(launch_stream_gemm(p.w_dtype, p.act_dtype, kGemmDown, g2, (int)(p.K / 128), s));
+    MOE_HIP(launch_stream_gemm(p.w_dtype, p.act_dtype, kGemmDown, g2, (int)(p.K / 128),
+                               stream_gemm_down_blocks(p.w_dtype, p.E, p.M * p.topk, p.K, I), s));
   else if (big)
     MOE_HIP(launch_mfma_gemm(kGemmDown, g2, mfma_gemm_n_tiles(kGemmDown, g2.Nw), s));
   else

@@ -186,8 +186,11 @@ hipError_t launch_grouped_gemm(int w_dtype, int out_dtype, GemmKind kind, const 
 // columns, down tiles 128 output columns; rows per tile below.
 int stream_gemm_tile_rows(int w_dtype);
 bool stream_gemm_fits(int w_dtype, int64_t K, int64_t I);
+// 16-row weight blocks per wavefront for the down GEMM (1 or 2), from the
+// problem's shape: two when that still leaves enough work items.
+int stream_gemm_down_blocks(int w_dtype, int64_t E, int64_t pairs, int64_t K, int64_t I);
 hipError_t launch_stream_gemm(int w_dtype, int out_dtype, GemmKind kind, const GemmParams &g, int n_tiles,
-                              hipStream_t s);
+                              int down_blocks, hipStream_t s);
 // Compute-bound variant (bf16, many rows per expert): 256-row tiles; gated
 // tiles cover 128 act columns, down tiles 256 output columns.
 int mfma_gemm_tile_rows();

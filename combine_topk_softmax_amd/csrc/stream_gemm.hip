@@ -28,6 +28,8 @@
 // q = lane/16 holds 32 contiguous bytes; MFMA step t takes bytes
 // [t*F, t*F + F) of them (F = 16 for bf16, 8 for fp8).  A and B use the same
 // mapping, so the k permutation this implies cancels in the dot product.
+#include <algorithm>
+
 #include "moe_device.h"
 
 namespace moe {
@@ -365,6 +367,17 @@ int stream_gemm_tile_rows(int w_dtype) { return w_dtype == MOE_DTYPE_FP8_E4M3 ? 
 #define MOE_STREAM_DOWN_D_FP8 4
 #endif
 
+// Down GEMM: 16-row weight blocks per wavefront.  Each wavefront reads the
+// whole activation tile from LDS once per K-step, so two blocks halve the LDS
+// bytes read per weight byte -- but also halve the number of work items, so
+// the host keeps one block when two would leave CUs idle.
+#ifndef MOE_STREAM_DOWN2_D_BF16
+#define MOE_STREAM_DOWN2_D_BF16 2
+#endif
+#ifndef MOE_STREAM_DOWN2_D_FP8
+#define MOE_STREAM_DOWN2_D_FP8 2
+#endif
+
 constexpr int unroll_of(int d) { return d % 2 == 0 ? d : 2 * d; }
 
 bool stream_gemm_fits(int w_dtype, int64_t K, int64_t I) {
@@ -375,12 +388,24 @@ bool stream_gemm_fits(int w_dtype, int64_t K, int64_t I) {
   return I % 128 == 0 && (K * eb / 128) % ug == 0 && (I * eb / 128) % ud == 0;
 }
 
+int stream_gemm_down_blocks(int w_dtype, int64_t E, int64_t pairs, int64_t K, int64_t I) {
+  const bool fp8 = w_dtype == MOE_DTYPE_FP8_E4M3;
+  const int eb = fp8 ? 1 : 2;
+  const int u2 = unroll_of(fp8 ? MOE_STREAM_DOWN2_D_FP8 : MOE_STREAM_DOWN2_D_BF16);
+  const int64_t items = std::min(E, pairs) * (K / 256);   // at most one row tile per expert
+  return K % 256 == 0 && (I * eb / 128) % u2 == 0 && items >= 512 ? 2 : 1;
+}
+
 hipError_t launch_stream_gemm(int w_dtype, int out_dtype, GemmKind kind, const GemmParams &g, int n_tiles,
-                              hipStream_t s) {
+                              int down_blocks, hipStream_t s) {
   const bool fp8 = w_dtype == MOE_DTYPE_FP8_E4M3;
   if (kind == kGemmGatedAct)
     return fp8 ? launch_cfg<1, true, 2, MOE_STREAM_GATED_D_FP8, 128>(out_dtype, g, n_tiles, s)
                : launch_cfg<2, true, 2, MOE_STREAM_GATED_D_BF16, 256>(out_dtype, g, n_tiles, s);
+  // down: n_tiles = K / 128 from the caller, K / 256 with two blocks per wavefront
+  if (down_blocks == 2)
+    return fp8 ? launch_cfg<1, false, 2, MOE_STREAM_DOWN2_D_FP8, 128>(out_dtype, g, n_tiles / 2, s)
+               : launch_cfg<2, false, 2, MOE_STREAM_DOWN2_D_BF16, 256>(out_dtype, g, n_tiles / 2, s);
   return fp8 ? launch_cfg<1, false, 1, MOE_STREAM_DOWN_D_FP8, 128>(out_dtype, g, n_tiles, s)
              : launch_cfg<2, false, 1, MOE_STREAM_DOWN_D_BF16, 256>(out_dtype, g, n_tiles, s);
 }

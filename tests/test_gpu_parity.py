@@ -171,6 +171,11 @@ SMALL = {
     "bf16_mfma_batched": WORKLOADS["mixtral_bf16"].replace(M=600, K=256, I=128, E=3, topk=2,
                                                            format=FORMAT_BATCHED, capacity=600,
                                                            logits_dist="normal"),
+    # weight streaming with enough (expert, column tile) items that the down
+    # GEMM gives each wavefront two 16-row weight blocks
+    "bf16_down2": WORKLOADS["mixtral_bf16"].replace(M=256, K=2048, I=128, E=64, topk=4, renormalize=False,
+                                                    logits_dist="normal"),
+    "fp8_batched_down2": WORKLOADS["decode_fp8_m64"].replace(M=96, K=2048, I=256, E=64, topk=4, capacity=96),
     # the same regime with I % 128 != 0: the general 128 x 128 tile kernel
     "bf16_tiled_I192": WORKLOADS["mixtral_bf16"].replace(M=700, K=384, I=192, E=4, topk=2, renormalize=False,
                                                          logits_dist="normal"),
