@@ -66,32 +66,33 @@ __device__ __forceinline__ int swz(int row, int b) {
   return row * 128 + ((((b >> 4) ^ ((row >> 1) & 7)) << 4) | (b & 15));
 }
 
+// Staging registers are native vectors: HIP's uint4 is a struct whose copies
+// become memcpy, which can keep a staging array in memory.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
 template <typename F>
-__device__ __forceinline__ F frag_at(const uint4 (&v)[2], int t) {
+__device__ __forceinline__ F frag_at(const u32x4 (&v)[2], int t) {
   if constexpr (sizeof(F) == 16) {
     return __builtin_bit_cast(F, v[t]);
   } else {
-    const uint4 q = v[t >> 1];
-    const uint2 h = (t & 1) ? make_uint2(q.z, q.w) : make_uint2(q.x, q.y);
+    const u32x4 q = v[t >> 1];
+    const u32x2 h = (t & 1) ? q.zw : q.xy;
     return __builtin_bit_cast(F, h);
   }
 }
 
 constexpr int kThreads = 512;
 
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
 // 16-byte weight load; packed weights stream once in whole cache lines, so
 // they are read non-temporally (the row-major pattern touches half lines per
 // instruction and is faster through the cache).
 template <bool NT>
-__device__ __forceinline__ uint4 load_w16(const uint8_t *p) {
-  if constexpr (NT) {
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
-  } else {
-    return *reinterpret_cast<const uint4 *>(p);
-  }
+__device__ __forceinline__ u32x4 load_w16(const uint8_t *p) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  else
+    return *reinterpret_cast<const u32x4 *>(p);
 }
 
 template <int EB, bool GATED, bool OUT_BF16, int NBW, int D, int TMAX, bool PACKED>
@@ -143,19 +144,15 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
       wsrc[b] = reinterpret_cast<const uint8_t *>(g.w) + ((int64_t)e * g.Nw + wrow0 + r16) * row_bytes + q * 32;
     wscale[b] = kScaled ? g.w_scale + ((int64_t)e * (g.Nw / 128) + wrow0 / 128) * kblocks : nullptr;
   }
-  // A row (in the activation tensor) of tile row r; rows past the count map to
-  // the last real row so that their loads share its cache lines.
-  auto a_row_of = [&](int r, bool &ok) -> int64_t {
-    const int rc = min(r, T - 1);
-    const int64_t s = row0 + rc;
-    ok = r < T;
+  // A row (in the activation tensor) of tile row r.  Rows past the count map
+  // to the last real row (so their loads share its cache lines) and padding
+  // slots to row 0: an A row only feeds its own output row, which the
+  // epilogue does not store for those rows, so no mask is needed.
+  auto a_row_of = [&](int r) -> int64_t {
+    const int64_t s = row0 + min(r, T - 1);
     if (!g.perm) return s;
     const int f = g.perm[s];
-    if (f < 0 || f >= g.n_pairs) {
-      ok = false;
-      return 0;
-    }
-    return f / g.topk;
+    return (f < 0 || f >= g.n_pairs) ? 0 : f / g.topk;
   };
   const int ach = tid & 7;
   const uint8_t *abase = reinterpret_cast<const uint8_t *>(g.a) + ach * 16;
@@ -165,31 +162,29 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
   auto body = [&]<int NMB>() {
     constexpr int kPasses = (NMB * 16 + 63) / 64;   // A rows per thread per K-step
     int64_t arow[kPasses];
-    bool aok[kPasses];
 #pragma unroll
-    for (int i = 0; i < kPasses; ++i) arow[i] = a_row_of((tid >> 3) + 64 * i, aok[i]);
-    bool sok = false;
-    const int64_t srow = kScaled ? a_row_of(tid, sok) : 0;
+    for (int i = 0; i < kPasses; ++i) arow[i] = a_row_of((tid >> 3) + 64 * i);
+    const int64_t srow = kScaled ? a_row_of(tid) : 0;
 
-    uint4 ra[2][kPasses];
+    u32x4 ra[2][kPasses];
     float rsa[2] = {0.0f, 0.0f};
     auto loadA = [&](int j, int ks) {
 #pragma unroll
       for (int i = 0; i < kPasses; ++i)
-        ra[j][i] = *reinterpret_cast<const uint4 *>(abase + arow[i] * row_bytes + (int64_t)ks * 128);
+        ra[j][i] = *reinterpret_cast<const u32x4 *>(abase + arow[i] * row_bytes + (int64_t)ks * 128);
       if constexpr (kScaled) rsa[j] = g.a_scale[srow * kblocks + ks];
     };
     auto storeA = [&](int j, int st) {
 #pragma unroll
       for (int i = 0; i < kPasses; ++i) {
         const int r = (tid >> 3) + 64 * i;
-        *reinterpret_cast<uint4 *>(&As[st][swz(r, ach * 16)]) = aok[i] ? ra[j][i] : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<u32x4 *>(&As[st][swz(r, ach * 16)]) = ra[j][i];
       }
       if constexpr (kScaled)
-        if (tid < TMAX) Sa[st][tid] = sok ? rsa[j] : 0.0f;
+        if (tid < TMAX) Sa[st][tid] = rsa[j];
     };
 
-    uint4 wb[D][NBW][2];
+    u32x4 wb[D][NBW][2];
     float wsv[D][NBW];
     auto loadW = [&](int j, int ks) {
 #pragma unroll
