@@ -66,7 +66,8 @@ def gemm1_algorithmic(wl, counts):
     if wl.w_dtype == 2:
         w_bytes += active * (2 * wl.I // 128) * (wl.K // 128) * 4
     x_bytes = wl.M * wl.K * eb_a
-    act_bytes = wl.M * wl.topk * wl.I * (4 if wl.w_dtype == 2 else eb_a)
+    # act is written once: bf16 / fp32, or (fp8) e4m3 codes plus one fp32 scale per 128 columns
+    act_bytes = wl.M * wl.topk * (wl.I + wl.I // 128 * 4 if wl.w_dtype == 2 else wl.I * eb_a)
     flops = 2 * wl.M * wl.topk * 2 * wl.I * wl.K
     return w_bytes + x_bytes + act_bytes, flops
 

@@ -235,8 +235,10 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const float *__restrict
   const int64_t row0 = (int64_t)d[1] + d[2];
   const int nrows = d[3];
   const int G = (int)(cols / 128);
-  const int team = threadIdx.x >> 4, tl = threadIdx.x & 15;
-  for (int pidx = team; pidx < nrows * G; pidx += 16) {
+  // gridDim.y blocks share a tile's (row, group) items, 16 teams each
+  const int team = blockIdx.y * 16 + (threadIdx.x >> 4), tl = threadIdx.x & 15;
+  const int teams = gridDim.y * 16;
+  for (int pidx = team; pidx < nrows * G; pidx += teams) {
     const int64_t row = row0 + pidx / G;
     const int g = pidx % G;
     const float4 *src = reinterpret_cast<const float4 *>(in + row * cols + g * 128 + tl * 8);
@@ -354,7 +356,8 @@ hipError_t launch_dispatch_rows(const moe_problem &p, const void *x, const int32
 
 hipError_t launch_quant_rows(const float *in, const int32_t *tiles, int max_tiles, int64_t cols,
                              uint8_t *q, float *scale, hipStream_t s) {
-  quant_rows_kernel<<<(unsigned)max_tiles, 256, 0, s>>>(in, tiles, max_tiles, cols, q, scale);
+  const dim3 grid((unsigned)max_tiles, 8);
+  quant_rows_kernel<<<grid, 256, 0, s>>>(in, tiles, max_tiles, cols, q, scale);
   return hipGetLastError();
 }
 

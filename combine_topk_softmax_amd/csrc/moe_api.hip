@@ -193,6 +193,11 @@ moe_status do_experts(const moe_problem &p, const void *a, const float *a_scale,
   g1.half_n = I;
   g1.w_packed = p.weight_layout == MOE_WEIGHTS_PACKED;
   g1.t = gt;
+  if (streaming && fp8) {
+    // the gated GEMM quantises act itself (one 128-column group per tile)
+    g1.out = at<void>(ws, L.act_q);
+    g1.out_scale = at<float>(ws, L.act_scale);
+  }
   if (streaming)
     MOE_HIP(launch_stream_gemm(p.w_dtype, fp8 ? MOE_DTYPE_F32 : p.act_dtype, kGemmGatedAct, g1,
                                (int)(I / 128), 1, s));
@@ -202,7 +207,7 @@ moe_status do_experts(const moe_problem &p, const void *a, const float *a_scale,
     MOE_HIP(launch_grouped_gemm(p.w_dtype, fp8 ? MOE_DTYPE_F32 : p.act_dtype, kGemmGatedAct, g1,
                                 (int)(I / 64), s));
   record(ev, 3, s);
-  if (fp8)
+  if (fp8 && !streaming)
     MOE_HIP(launch_quant_rows(at<float>(ws, L.act), tiles, (int)L.max_tiles, I, at<uint8_t>(ws, L.act_q),
                               at<float>(ws, L.act_scale), s));
 

@@ -158,6 +158,8 @@ struct GemmParams {
   void *out;
   int64_t ldo;
   const int32_t *out_perm;    // down GEMM: slot -> output row; NULL: row = slot
+  float *out_scale;           // gated fp8 streaming GEMM: if set, act is written as e4m3 codes
+                              // (out, ldo bytes per row) with one scale per row and 128 columns
   int64_t half_n;             // gated: I (up rows start here)
   int w_packed;               // weights in MOE_WEIGHTS_PACKED order
   GemmTiles t;

@@ -157,6 +157,53 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
   const int ach = tid & 7;
   const uint8_t *abase = reinterpret_cast<const uint8_t *>(g.a) + ach * 16;
 
+  // Gated fp8: the act tile's 128 columns are exactly one quantisation group,
+  // so the epilogue quantises it directly (the per-token-group e4m3 scheme
+  // that the layer applies to its input, applied again to act before the down
+  // GEMM): row maxima are reduced across the 16 lanes holding a row's columns
+  // in a wavefront, then across the 8 wavefronts through LDS; the codes are
+  // staged in LDS and written as whole 128-byte rows.
+  auto quant_epilogue = [&]<int NMB>(f32x4 (&acc)[NMB][2]) {
+    __syncthreads();   // every wavefront is done reading the A tiles
+    float *rmax = reinterpret_cast<float *>(&As[0][0]);   // [TMAX][8]
+    uint8_t *codes = &As[1][0];                           // [TMAX][128]
+    float v[NMB][4];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float gt = acc[mb][0][i], up = acc[mb][1][i];
+        v[mb][i] = gt / (1.0f + expf(-gt)) * up;
+        float m = fabsf(v[mb][i]);
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
+        if (r16 == 0) rmax[(mb * 16 + q * 4 + i) * 8 + wv] = m;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = mb * 16 + q * 4 + i;
+        float amax = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) amax = fmaxf(amax, rmax[r * 8 + w]);
+        const float sc = group_scale(amax);
+        codes[r * 128 + wv * 16 + r16] = (uint8_t)quant_e4m3(v[mb][i], sc);
+        if (wv == 0 && r16 == 0 && r < T) g.out_scale[(row0 + r) * (g.ldo / 128) + nt] = sc;
+      }
+    }
+    __syncthreads();
+    // 8 threads per row, 16 bytes each
+    for (int c = tid; c < NMB * 16 * 8; c += kThreads) {
+      const int r = c >> 3, b = (c & 7) * 16;
+      if (r < T)
+        *reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(g.out) + (row0 + r) * g.ldo + (int64_t)nt * 128 + b) =
+            *reinterpret_cast<const u32x4 *>(&codes[r * 128 + b]);
+    }
+  };
+
   // The main loop for NMB blocks of 16 rows (NMB * 16 >= T): every load, LDS
   // access and MFMA is unconditional.
   auto body = [&]<int NMB>() {
@@ -271,6 +318,12 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
     }
 
     // Epilogue: in a 16x16 block, lane holds column r16 of rows 4*q + i.
+    if constexpr (GATED && kScaled) {
+      if (g.out_scale) {
+        quant_epilogue.template operator()<NMB>(acc);
+        return;
+      }
+    }
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll

@@ -247,6 +247,43 @@ def test_shared_expert_parity(M, K, Is):
     assert err <= U.tol_for(wl)
 
 
+@pytest.mark.parametrize("name", ["fp8_batched", "fp8_standard"])
+def test_act_requant_group_invariants(name):
+    """fp8: the gated GEMM writes act as e4m3 codes with one scale per row and
+    128 columns, the scale being the group's max magnitude / 448.  So every
+    group of a real row holds a code of magnitude exactly 448 and no larger
+    one, and every scale is positive."""
+    wl = SMALL[name]
+    d = make_inputs(wl, seed=17, device="cpu")
+    ids, _ = _ids_from_oracle(wl)
+    p = U.problem(wl)
+    ws = moe.empty_workspace(p)
+    g = U.to_cuda(d)
+    counts = torch.empty(wl.E, dtype=torch.int32, device="cuda")
+    bat = U.batched(wl)
+    rows_a = wl.E * wl.capacity if bat else wl.M
+    a_out = torch.empty(*((wl.E, wl.capacity) if bat else (wl.M,)), wl.K, dtype=torch.uint8, device="cuda")
+    a_scale = torch.empty(rows_a, wl.K // 128, device="cuda")
+    moe.moe_prepare(p, g["x"], torch.from_numpy(ids).cuda(), a_out, a_scale, counts, ws)
+    rows = wl.E * wl.capacity if bat else wl.M * wl.topk
+    fused = torch.empty(rows, wl.K, dtype=torch.bfloat16, device="cuda")
+    moe.moe_experts(p, a_out, a_scale, g["w1"], g["w1_scale"], g["w2"], g["w2_scale"], counts, fused, ws)
+    torch.cuda.synchronize()
+    L = moe.workspace_layout(p)
+    G = wl.I // 128
+    codes = U.ws_view(ws, L.act_q, L.act_rows * wl.I, torch.uint8).cpu().numpy().reshape(L.act_rows, G, 128)
+    scales = U.ws_view(ws, L.act_scale, L.act_rows * G, torch.float32).cpu().numpy().reshape(L.act_rows, G)
+    c = counts.cpu().numpy()
+    if bat:
+        real = np.concatenate([e * wl.capacity + np.arange(c[e]) for e in range(wl.E)])
+    else:
+        real = np.arange(wl.M * wl.topk)       # every slot of the permutation is a real pair (align 1)
+    mags = np.abs(oracle.e4m3_decode(codes[real].ravel()).reshape(len(real), G, 128))
+    assert len(real) > 0
+    np.testing.assert_array_equal(mags.max(axis=2), 448.0)
+    assert np.all(scales[real] > 0)
+
+
 def test_finalize_parity():
     for wl, bat in ((WORKLOADS["tiny_fp32"], False), (SMALL["bf16_ragged"], False), (SMALL["fp8_batched"], True)):
         gen = torch.Generator().manual_seed(15)
