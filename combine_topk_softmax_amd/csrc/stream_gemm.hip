@@ -23,11 +23,12 @@
 //  * work items are dealt out XCD by XCD: consecutive items of one expert land
 //    on the same XCD, so its activation rows stay in that XCD's L2.
 //
-// MFMA: v_mfma_f32_16x16x32_bf16 or _fp8_fp8 (OCP e4m3; fp32 block scales
-// applied per 128-wide K block).  Inside each 128-byte K-step a lane of group
-// q = lane/16 holds 32 contiguous bytes; MFMA step t takes bytes
-// [t*F, t*F + F) of them (F = 16 for bf16, 8 for fp8).  A and B use the same
-// mapping, so the k permutation this implies cancels in the dot product.
+// MFMA: v_mfma_f32_16x16x32_bf16, or for fp8 v_mfma_scale_f32_16x16x128_f8f6f4
+// with unit block scales (OCP e4m3; the layer's fp32 block scales applied per
+// 128-wide K block).  Inside each 128-byte K-step a lane of group q = lane/16
+// holds 32 contiguous bytes; MFMA step t takes bytes [t*F, t*F + F) of them
+// (F = 16 for bf16: two steps; F = 32 for fp8: one step).  A and B use the
+// same mapping, so the k permutation this implies cancels in the dot product.
 #include <algorithm>
 
 #include "moe_device.h"
@@ -50,12 +51,19 @@ struct Mfma16<2> {
   }
 };
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// fp8: gfx950's 16x16x128 MFMA takes a whole 128-byte K-step per instruction
+// (a lane's 32 bytes of its row), four times the K of the 16x16x32 form.  It
+// exists only with per-32-element E8M0 block scales; 127 encodes 2^0, so the
+// product is the plain e4m3 one (format 0 = OCP e4m3 for both operands) and
+// the layer's fp32 scales are applied per 128-wide K block as before.
 template <>
 struct Mfma16<1> {
-  static constexpr int kSteps = 4;
-  typedef long frag;
+  static constexpr int kSteps = 1;
+  typedef i32x8 frag;
   __device__ static f32x4 mma(frag a, frag b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
   }
 };
 
@@ -73,7 +81,9 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 template <typename F>
 __device__ __forceinline__ F frag_at(const u32x4 (&v)[2], int t) {
-  if constexpr (sizeof(F) == 16) {
+  if constexpr (sizeof(F) == 32) {
+    return __builtin_bit_cast(F, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
+  } else if constexpr (sizeof(F) == 16) {
     return __builtin_bit_cast(F, v[t]);
   } else {
     const u32x4 q = v[t >> 1];
@@ -82,7 +92,23 @@ __device__ __forceinline__ F frag_at(const u32x4 (&v)[2], int t) {
   }
 }
 
+// A fragment from the swizzled LDS tile: bytes [off, off + sizeof(F)) of a row;
+// a 32-byte fragment spans two 16-byte chunks, which the swizzle places apart.
+template <typename F>
+__device__ __forceinline__ F lds_frag(const uint8_t *A, int row, int off) {
+  if constexpr (sizeof(F) == 32) {
+    const u32x4 lo = *reinterpret_cast<const u32x4 *>(A + swz(row, off));
+    const u32x4 hi = *reinterpret_cast<const u32x4 *>(A + swz(row, off + 16));
+    return __builtin_bit_cast(F, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  } else {
+    return *reinterpret_cast<const F *>(A + swz(row, off));
+  }
+}
+
 constexpr int kThreads = 512;
+#ifndef MOE_STREAM_FRAG_AHEAD
+#define MOE_STREAM_FRAG_AHEAD 2
+#endif
 
 // 16-byte weight load; packed weights stream once in whole cache lines, so
 // they are read non-temporally (the row-major pattern touches half lines per
@@ -249,40 +275,49 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
 #pragma unroll
       for (int b = 0; b < NBW; ++b) acc[mb][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // One K-step of MFMAs; the next block's A fragments are read from LDS
-    // before the current block's MFMAs so that LDS latency hides behind them.
+    // One K-step of MFMAs from LDS stage st and weight registers j.
     auto compute = [&](int st, int j) {
       const uint8_t *A = As[st];
-      frag an[MM::kSteps];
+      if constexpr (!kScaled && MM::kSteps > 1) {
+        // Sub-step outermost, so the MFMAs into one accumulator are NMB * NBW
+        // instructions apart; A fragments are read kAhead (sub-step, block)
+        // positions ahead of their MFMAs to cover LDS latency (the fully
+        // unrolled ring keeps kAhead + 1 fragments live).
+        constexpr int S = MM::kSteps * NMB;
+        constexpr int kAhead = MOE_STREAM_FRAG_AHEAD < S ? MOE_STREAM_FRAG_AHEAD : S;
+        frag f[S];
 #pragma unroll
-      for (int t = 0; t < MM::kSteps; ++t)
-        an[t] = *reinterpret_cast<const frag *>(A + swz(r16, q * 32 + t * kFrag));
+        for (int x = 0; x < kAhead; ++x) f[x] = lds_frag<frag>(A, (x % NMB) * 16 + r16, q * 32 + (x / NMB) * kFrag);
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) {
-        frag ac[MM::kSteps];
-#pragma unroll
-        for (int t = 0; t < MM::kSteps; ++t) ac[t] = an[t];
-        if (mb + 1 < NMB) {
-#pragma unroll
-          for (int t = 0; t < MM::kSteps; ++t)
-            an[t] = *reinterpret_cast<const frag *>(A + swz((mb + 1) * 16 + r16, q * 32 + t * kFrag));
-        }
-        f32x4 part[NBW];
-        if constexpr (kScaled)
-#pragma unroll
-          for (int b = 0; b < NBW; ++b) part[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int t = 0; t < MM::kSteps; ++t) {
-#pragma unroll
-          for (int b = 0; b < NBW; ++b) {
-            const frag bf = frag_at<frag>(wb[j][b], t);
-            if constexpr (kScaled)
-              part[b] = MM::mma(ac[t], bf, part[b]);
-            else
-              acc[mb][b] = MM::mma(ac[t], bf, acc[mb][b]);
+        for (int x = 0; x < S; ++x) {
+          if (x + kAhead < S) {
+            const int y = x + kAhead;
+            f[y] = lds_frag<frag>(A, (y % NMB) * 16 + r16, q * 32 + (y / NMB) * kFrag);
           }
+          const int mb = x % NMB, t = x / NMB;
+#pragma unroll
+          for (int b = 0; b < NBW; ++b) acc[mb][b] = MM::mma(f[x], frag_at<frag>(wb[j][b], t), acc[mb][b]);
+          // keep the read-ahead in place (the scheduler would otherwise move
+          // each read next to its MFMAs and wait for it there)
+          __builtin_amdgcn_sched_barrier(0);
         }
-        if constexpr (kScaled) {
+      } else {
+        // fp8: one MFMA step per K-step and block.  Blocks in order, A fragments
+        // read kAhead blocks ahead (pinned like the bf16 ring), each block's
+        // partial sums scaled by its row and weight-block scales right after
+        // its MFMAs.
+        static_assert(MM::kSteps == 1, "scaled path: one MFMA step per K-step");
+        constexpr int kAhead = MOE_STREAM_FRAG_AHEAD < NMB ? MOE_STREAM_FRAG_AHEAD : NMB;
+        frag f[NMB];
+#pragma unroll
+        for (int x = 0; x < kAhead; ++x) f[x] = lds_frag<frag>(A, x * 16 + r16, q * 32);
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+          if (mb + kAhead < NMB) f[mb + kAhead] = lds_frag<frag>(A, (mb + kAhead) * 16 + r16, q * 32);
+          f32x4 part[NBW];
+#pragma unroll
+          for (int b = 0; b < NBW; ++b)
+            part[b] = MM::mma(f[mb], frag_at<frag>(wb[j][b], 0), f32x4{0.0f, 0.0f, 0.0f, 0.0f});
           const float4 sa4 = *reinterpret_cast<const float4 *>(&Sa[st][mb * 16 + q * 4]);
           const float sa[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
 #pragma unroll
@@ -294,6 +329,7 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
           // every block's partial sums live at once.
 #pragma unroll
           for (int b = 0; b < NBW; ++b) asm volatile("" : "+v"(acc[mb][b]));
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     };
