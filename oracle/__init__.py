@@ -21,6 +21,7 @@ _LIB = os.path.join(_HERE, "libmoe_oracle.so")
 F32, BF16, FP8 = 0, 1, 2
 SOFTMAX, SIGMOID = 0, 1
 STANDARD, BATCHED = 0, 1
+SILU, GELU = 0, 1
 
 
 def compile_source(src: str, out: str) -> str:
@@ -57,14 +58,14 @@ def load_library(path: str):
     L.oracle_permute_standard.restype = i64
     L.oracle_permute_standard.argtypes = [i64, vp, i64, i64, vp, vp, vp, i64, vp]
     L.oracle_permute_batched.argtypes = [i64, vp, i64, i64, vp, vp]
-    L.oracle_expert_row.argtypes = [i32, vp, vp, vp, vp, i64, i64, i64, dp, i32, dp, dp]
-    L.oracle_input_row.argtypes = [i32, i32, vp, i64, i64, dp]
+    L.oracle_expert_row.argtypes = [i32, vp, vp, vp, vp, i64, i64, i64, i32, dp, i32, dp, dp]
+    L.oracle_input_row.argtypes = [i32, i32, vp, i64, i64, i32, C.c_float, dp]
     L.oracle_combine.argtypes = [i64, i64, i64, dp, dp, vp, dp]
     L.oracle_moe_tokens.restype = i32
-    L.oracle_moe_tokens.argtypes = [i64, i64, i64, i64, i64, i32, i32, i32, i32, i32, i32,
-                                    i64, vp, vp, vp, vp, vp, vp, i64, vp, dp, vp, dp]
+    L.oracle_moe_tokens.argtypes = [i64, i64, i64, i64, i64, i64, i32, i32, i32, i32, i32, i32,
+                                    i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp, dp, vp, dp]
     L.oracle_dense_mlp_tokens.restype = i32
-    L.oracle_dense_mlp_tokens.argtypes = [i64, i64, i64, i32, vp, vp, vp, i64, vp, dp]
+    L.oracle_dense_mlp_tokens.argtypes = [i64, i64, i64, i32, i32, vp, vp, vp, i64, vp, dp]
     return L
 
 
@@ -173,16 +174,18 @@ def permute_batched(ids, E: int, cap: int):
     return counts, inv
 
 
-def input_row(x, m: int, act_dtype: int, act_quant: int = 0) -> np.ndarray:
+def input_row(x, m: int, act_dtype: int, act_quant: int = 0, weight: Optional[float] = None) -> np.ndarray:
+    """Token m's input row as the experts see it; weight: router weight applied on the input."""
     xa = _np(x)
     K = xa.shape[-1]
     a = np.empty(K, np.float64)
-    lib().oracle_input_row(act_dtype, act_quant, _p(xa), K, m, _p(a))
+    lib().oracle_input_row(act_dtype, act_quant, _p(xa), K, m, int(weight is not None),
+                           0.0 if weight is None else float(weight), _p(a))
     return a
 
 
 def expert_row(a, e: int, w1, w2, w_dtype: int, I: int, w1_scale=None, w2_scale=None,
-               requant_fp8: bool = False):
+               requant_fp8: bool = False, activation: int = SILU):
     """Returns (act[I] before any re-quantisation, y[K])."""
     a = np.ascontiguousarray(a, dtype=np.float64)
     K = a.size
@@ -191,7 +194,7 @@ def expert_row(a, e: int, w1, w2, w_dtype: int, I: int, w1_scale=None, w2_scale=
     s2 = _np(w2_scale, np.float32)
     act = np.empty(I, np.float64)
     y = np.empty(K, np.float64)
-    lib().oracle_expert_row(w_dtype, _p(w1a), _p(s1), _p(w2a), _p(s2), e, K, I, _p(a),
+    lib().oracle_expert_row(w_dtype, _p(w1a), _p(s1), _p(w2a), _p(s2), e, K, I, activation, _p(a),
                             int(requant_fp8), _p(act), _p(y))
     return act, y
 
@@ -211,7 +214,9 @@ def combine(w, y, keep=None) -> np.ndarray:
 def moe_tokens(wl, inputs: dict, tokens=None):
     """The whole layer for the given token rows of a workload.
 
-    Returns (out [ntok, K] float64, ids [ntok, k], weights [ntok, k])."""
+    inputs may hold "expert_map" (int32 [global experts], local index or -1)
+    for one expert-parallel shard; wl.global_E (0: wl.E) is the router width.
+    Returns (out [ntok, K] float64, ids [ntok, k] global, weights [ntok, k])."""
     logits = np.ascontiguousarray(_np(inputs["logits"]), dtype=np.float32)
     x = _np(inputs["x"])
     w1, w2 = _np(inputs["w1"]), _np(inputs["w2"])
@@ -223,23 +228,30 @@ def moe_tokens(wl, inputs: dict, tokens=None):
     out = np.empty((tok.size, wl.K), np.float64)
     ids = np.empty((tok.size, wl.topk), np.int32)
     wts = np.empty((tok.size, wl.topk), np.float64)
-    rc = lib().oracle_moe_tokens(M, wl.K, wl.I, wl.E, wl.topk, wl.scoring, int(wl.renormalize),
+    emap = _np(inputs.get("expert_map"), np.int32)
+    Eg = getattr(wl, "global_E", 0) or wl.E
+    assert logits.shape[1] == Eg and (emap is None or emap.size == Eg)
+    rc = lib().oracle_moe_tokens(M, wl.K, wl.I, wl.E, Eg, wl.topk, wl.scoring, int(wl.renormalize),
                                  wl.act_dtype, wl.w_dtype, wl.act_quant, wl.format,
-                                 wl.capacity, _p(logits), _p(x), _p(w1), _p(s1), _p(w2), _p(s2),
+                                 wl.capacity, getattr(wl, "activation", SILU),
+                                 int(getattr(wl, "router_weight_on_input", False)), _p(emap),
+                                 _p(logits), _p(x), _p(w1), _p(s1), _p(w2), _p(s2),
                                  tok.size, _p(tok), _p(out), _p(ids), _p(wts))
+    if rc == -2:
+        raise ValueError("router weight on the input needs topk == 1")
     if rc != 0:
         raise ValueError("token index out of range")
     return out, ids, wts
 
 
-def dense_mlp_tokens(x, w1, w2, I: int, dtype: int, tokens=None) -> np.ndarray:
+def dense_mlp_tokens(x, w1, w2, I: int, dtype: int, tokens=None, activation: int = SILU) -> np.ndarray:
     xa, w1a, w2a = _np(x), _np(w1), _np(w2)
     M, K = xa.shape
     if tokens is None:
         tokens = list(range(M))
     tok = np.ascontiguousarray(tokens, dtype=np.int64)
     out = np.empty((tok.size, K), np.float64)
-    rc = lib().oracle_dense_mlp_tokens(M, K, I, dtype, _p(xa), _p(w1a), _p(w2a), tok.size,
+    rc = lib().oracle_dense_mlp_tokens(M, K, I, dtype, activation, _p(xa), _p(w1a), _p(w2a), tok.size,
                                        _p(tok), _p(out))
     if rc != 0:
         raise ValueError("token index out of range")

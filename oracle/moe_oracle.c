@@ -35,6 +35,15 @@
  *    slots hold -1; inside a segment pairs keep ascending flat index m*k+j.
  *  - Batched layout: a pair's slot is its rank among the pairs of its expert
  *    (ascending flat index); ranks >= capacity are dropped.
+ *  - gelu_and_mul: the exact GELU, g * Phi(g) = 0.5 g (1 + erf(g / sqrt 2)).
+ *  - Expert-parallel shard (expert_map: global -> local expert, -1 = held by
+ *    another shard): the router runs over the global experts; pairs of other
+ *    shards are neither counted nor computed and add nothing to this shard's
+ *    output, so the shards' outputs sum to the unsharded layer's.
+ *  - Router weight on the input (topk = 1): the weight multiplies the input
+ *    row, which is then held in the activation dtype (the exact product
+ *    rounded to fp32, and to bf16 for bf16 activations) before any
+ *    quantisation; the combine then adds the expert output unweighted.
  *
  * Parity unpinned (conventions the pages leave open, shared by both sides):
  * the gate/up half order, the 1e-10 floor in the fp8 scale and the Zipf
@@ -48,6 +57,7 @@
 enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8 = 2 };
 enum { OR_SOFTMAX = 0, OR_SIGMOID = 1 };
 enum { OR_STANDARD = 0, OR_BATCHED = 1 };
+enum { OR_SILU = 0, OR_GELU = 1 };
 
 /* ---------------------------------------------------------------- formats */
 
@@ -187,10 +197,13 @@ void oracle_route(int64_t M, int64_t E, int64_t k, const float *logits, int scor
 
 /* ------------------------------------------------- counting and permutation */
 
-/* ExpertTokensMetadata.expert_num_tokens ([MK]): tokens routed to each expert. */
+/* ExpertTokensMetadata.expert_num_tokens ([MK]): tokens routed to each
+ * (local) expert.  A negative id is a pair held by another expert-parallel
+ * shard and is not counted. */
 void oracle_count(int64_t n, const int32_t *ids, int64_t E, int32_t *counts) {
   for (int64_t e = 0; e < E; ++e) counts[e] = 0;
-  for (int64_t f = 0; f < n; ++f) counts[ids[f]]++;
+  for (int64_t f = 0; f < n; ++f)
+    if (ids[f] >= 0) counts[ids[f]]++;
 }
 
 /* Standard activation format ([MK] FusedMoEActivationFormat.Standard; the
@@ -210,6 +223,10 @@ int64_t oracle_permute_standard(int64_t n, const int32_t *ids, int64_t E, int64_
   int32_t *next = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
   for (int64_t e = 0; e < E; ++e) next[e] = offsets[e];
   for (int64_t f = 0; f < n; ++f) {
+    if (ids[f] < 0) {          /* another shard's pair: no slot */
+      inv[f] = -1;
+      continue;
+    }
     int32_t s = next[ids[f]]++;
     perm[s] = (int32_t)f;
     inv[f] = s;
@@ -228,6 +245,10 @@ void oracle_permute_batched(int64_t n, const int32_t *ids, int64_t E, int64_t ca
   for (int64_t e = 0; e < E; ++e) counts[e] = 0;
   for (int64_t f = 0; f < n; ++f) {
     int32_t e = ids[f];
+    if (e < 0) {               /* another shard's pair */
+      inv[f] = -1;
+      continue;
+    }
     int32_t r = counts[e]++;
     inv[f] = r < cap ? (int32_t)(e * cap + r) : -1;
   }
@@ -240,12 +261,13 @@ void oracle_permute_batched(int64_t n, const int32_t *ids, int64_t E, int64_t ca
  * whose output is half the width of its input).
  *   h   = W1[e] a            (2I values; gate = h[0:I], up = h[I:2I])
  *   act = silu(gate) * up,   silu(z) = z / (1 + exp(-z))
+ *      or gelu(gate) * up,   gelu(z) = 0.5 z (1 + erf(z / sqrt 2))  (gelu_and_mul)
  *   [fp8: act is re-quantised per group of 128 before the second GEMM]
  *   y   = W2[e] act          (K values)
  * a is [K]; act_out [I] receives act before any re-quantisation. */
 void oracle_expert_row(int w_dtype, const void *w1, const float *w1_scale, const void *w2,
-                       const float *w2_scale, int64_t e, int64_t K, int64_t I, const double *a,
-                       int requant_fp8, double *act_out, double *y_out) {
+                       const float *w2_scale, int64_t e, int64_t K, int64_t I, int activation,
+                       const double *a, int requant_fp8, double *act_out, double *y_out) {
   double *act = (double *)malloc(sizeof(double) * (size_t)I);
 #pragma omp parallel for schedule(static)
   for (int64_t j = 0; j < I; ++j) {
@@ -254,7 +276,10 @@ void oracle_expert_row(int w_dtype, const void *w1, const float *w1_scale, const
       g += weight_at(w_dtype, w1, w1_scale, e, 2 * I, K, j, c) * a[c];
       u += weight_at(w_dtype, w1, w1_scale, e, 2 * I, K, I + j, c) * a[c];
     }
-    act[j] = g / (1.0 + exp(-g)) * u;
+    if (activation == OR_GELU)
+      act[j] = 0.5 * g * (1.0 + erf(g / sqrt(2.0))) * u;
+    else
+      act[j] = g / (1.0 + exp(-g)) * u;
   }
   if (act_out) memcpy(act_out, act, sizeof(double) * (size_t)I);
   if (requant_fp8) {
@@ -277,17 +302,42 @@ void oracle_expert_row(int w_dtype, const void *w1, const float *w1_scale, const
   free(act);
 }
 
-/* Input row of token m as the experts see it: x itself, or with token-group
- * fp8 quantisation the dequantised codes q*s ([MK] prepare). */
-void oracle_input_row(int act_dtype, int act_quant, const void *x, int64_t K, int64_t m, double *a) {
+/* bfloat16 round-to-nearest-even of a float32 (NaN kept quiet). */
+static float round_bf16(float v) {
+  uint32_t u;
+  memcpy(&u, &v, 4);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) u |= 0x00400000u;
+  else u += 0x7fffu + ((u >> 16) & 1u);
+  u &= 0xffff0000u;
+  float r;
+  memcpy(&r, &u, 4);
+  return r;
+}
+
+/* Element c of token m's input row: x itself, or with the router weight on
+ * the input ([MK] prepare: "apply the weights to the activations, before
+ * quantization + dispatching") w * x held in the activation dtype. */
+static double input_value(int act_dtype, const void *x, int64_t K, int64_t m, int64_t c, int weighted,
+                          float w) {
+  double v = act_at(act_dtype, x, m * K + c);
+  if (!weighted) return v;
+  float p = (float)((double)w * v);   /* exact product, one rounding to fp32 */
+  return act_dtype == OR_BF16 ? (double)round_bf16(p) : (double)p;
+}
+
+/* Input row of token m as the experts see it: x itself (weighted or not),
+ * or with token-group fp8 quantisation the dequantised codes q*s ([MK]
+ * prepare).  weighted != 0 applies router weight w to the input first. */
+void oracle_input_row(int act_dtype, int act_quant, const void *x, int64_t K, int64_t m, int weighted,
+                      float w, double *a) {
   if (!act_quant) {
-    for (int64_t c = 0; c < K; ++c) a[c] = act_at(act_dtype, x, m * K + c);
+    for (int64_t c = 0; c < K; ++c) a[c] = input_value(act_dtype, x, K, m, c, weighted, w);
     return;
   }
   float *xf = (float *)malloc(sizeof(float) * (size_t)K);
   uint8_t *q = (uint8_t *)malloc((size_t)K);
   float *s = (float *)malloc(sizeof(float) * (size_t)(K / 128));
-  for (int64_t c = 0; c < K; ++c) xf[c] = (float)act_at(act_dtype, x, m * K + c);
+  for (int64_t c = 0; c < K; ++c) xf[c] = (float)input_value(act_dtype, x, K, m, c, weighted, w);
   oracle_quant_g128(1, K, xf, q, s);
   for (int64_t c = 0; c < K; ++c) a[c] = oracle_e4m3_decode(q[c]) * (double)s[c / 128];
   free(xf);
@@ -315,45 +365,57 @@ void oracle_combine(int64_t M, int64_t k, int64_t K, const double *w, const doub
 /* --------------------------------------------------------------- layer */
 
 /* The whole layer ([MK] FusedMoEModularKernel.forward) for a chosen subset of
- * tokens: route all M tokens (the batched format needs every token's rank),
- * then for each chosen token run its k experts and combine.  out is
- * [ntok, K]; ids_out / w_out ([ntok, k]) may be NULL. */
-int oracle_moe_tokens(int64_t M, int64_t K, int64_t I, int64_t E, int64_t k, int scoring,
+ * tokens: route all M tokens over the Eg global experts (the batched format
+ * needs every token's rank), map each pick to a local expert (expert_map;
+ * NULL: global == local, Eg == E), then for each chosen token run the local
+ * experts of its picks and combine; picks held by other shards add nothing.
+ * weight_on_input (topk = 1): the router weight scales the input row and the
+ * combine adds the expert output unweighted.  out is [ntok, K]; ids_out /
+ * w_out ([ntok, k], global ids) may be NULL. */
+int oracle_moe_tokens(int64_t M, int64_t K, int64_t I, int64_t E, int64_t Eg, int64_t k, int scoring,
                       int renormalize, int act_dtype, int w_dtype, int act_quant, int format,
-                      int64_t cap, const float *logits, const void *x, const void *w1,
-                      const float *w1_scale, const void *w2, const float *w2_scale, int64_t ntok,
-                      const int64_t *tokens, double *out, int32_t *ids_out, double *w_out) {
+                      int64_t cap, int activation, int weight_on_input, const int32_t *expert_map,
+                      const float *logits, const void *x, const void *w1, const float *w1_scale,
+                      const void *w2, const float *w2_scale, int64_t ntok, const int64_t *tokens,
+                      double *out, int32_t *ids_out, double *w_out) {
   for (int64_t t = 0; t < ntok; ++t)
     if (tokens[t] < 0 || tokens[t] >= M) return -1;
+  if (weight_on_input && k != 1) return -2;
   int32_t *ids = (int32_t *)malloc(sizeof(int32_t) * (size_t)(M * k));
+  int32_t *lids = (int32_t *)malloc(sizeof(int32_t) * (size_t)(M * k));
   double *wts = (double *)malloc(sizeof(double) * (size_t)(M * k));
   int32_t *inv = NULL, *counts = NULL;
-  oracle_route(M, E, k, logits, scoring, renormalize, ids, wts);
+  oracle_route(M, Eg, k, logits, scoring, renormalize, ids, wts);
+  for (int64_t f = 0; f < M * k; ++f) lids[f] = expert_map ? expert_map[ids[f]] : ids[f];
   if (format == OR_BATCHED) {
     inv = (int32_t *)malloc(sizeof(int32_t) * (size_t)(M * k));
     counts = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
-    oracle_permute_batched(M * k, ids, E, cap, counts, inv);
+    oracle_permute_batched(M * k, lids, E, cap, counts, inv);
   }
   double *a = (double *)malloc(sizeof(double) * (size_t)K);
   double *y = (double *)malloc(sizeof(double) * (size_t)(k * K));
+  double *wc = (double *)malloc(sizeof(double) * (size_t)k);
   int32_t *keep = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
   for (int64_t t = 0; t < ntok; ++t) {
     int64_t m = tokens[t];
-    oracle_input_row(act_dtype, act_quant, x, K, m, a);
+    oracle_input_row(act_dtype, act_quant, x, K, m, weight_on_input, (float)wts[m * k], a);
     for (int64_t j = 0; j < k; ++j) {
       if (ids_out) ids_out[t * k + j] = ids[m * k + j];
       if (w_out) w_out[t * k + j] = wts[m * k + j];
-      keep[j] = !(inv && inv[m * k + j] < 0);
+      wc[j] = weight_on_input ? 1.0 : wts[m * k + j];
+      keep[j] = lids[m * k + j] >= 0 && !(inv && inv[m * k + j] < 0);
       if (keep[j])
-        oracle_expert_row(w_dtype, w1, w1_scale, w2, w2_scale, ids[m * k + j], K, I, a,
+        oracle_expert_row(w_dtype, w1, w1_scale, w2, w2_scale, lids[m * k + j], K, I, activation, a,
                           act_quant != 0, NULL, y + j * K);
     }
-    oracle_combine(1, k, K, wts + m * k, y, keep, out + t * K);
+    oracle_combine(1, k, K, wc, y, keep, out + t * K);
   }
   free(a);
   free(y);
+  free(wc);
   free(keep);
   free(ids);
+  free(lids);
   free(wts);
   free(inv);
   free(counts);
@@ -361,9 +423,9 @@ int oracle_moe_tokens(int64_t M, int64_t K, int64_t I, int64_t E, int64_t k, int
 }
 
 /* Shared expert ([SE]; [MK] forward returns (shared_output, output)): the
- * same gated MLP with one expert, applied to every token, not routed and not
- * weighted.  w1 [2I, K], w2 [K, I]; out [ntok, K]. */
-int oracle_dense_mlp_tokens(int64_t M, int64_t K, int64_t I, int dtype, const void *x,
+ * same gated MLP (same activation) with one expert, applied to every token,
+ * not routed and not weighted.  w1 [2I, K], w2 [K, I]; out [ntok, K]. */
+int oracle_dense_mlp_tokens(int64_t M, int64_t K, int64_t I, int dtype, int activation, const void *x,
                             const void *w1, const void *w2, int64_t ntok, const int64_t *tokens,
                             double *out) {
   for (int64_t t = 0; t < ntok; ++t)
@@ -371,8 +433,8 @@ int oracle_dense_mlp_tokens(int64_t M, int64_t K, int64_t I, int dtype, const vo
   double *a = (double *)malloc(sizeof(double) * (size_t)K);
   for (int64_t t = 0; t < ntok; ++t) {
     int64_t m = tokens[t];
-    oracle_input_row(dtype, 0, x, K, m, a);
-    oracle_expert_row(dtype, w1, NULL, w2, NULL, 0, K, I, a, 0, NULL, out + t * K);
+    oracle_input_row(dtype, 0, x, K, m, 0, 1.0f, a);
+    oracle_expert_row(dtype, w1, NULL, w2, NULL, 0, K, I, activation, a, 0, NULL, out + t * K);
   }
   free(a);
   return 0;

@@ -3,8 +3,8 @@
 It shares nothing with the oracle's code path: routing uses numpy's stable
 argsort and scipy's softmax / expit, every expert is applied densely to every
 token (no counting, permutation or combine step), SiLU is written as
-g * sigmoid(g), and the fp8 token-group quantiser uses torch's float8_e4m3fn
-cast.  Only suitable for tiny shapes.
+g * sigmoid(g) and GELU as g * Phi(g) with scipy's normal CDF, and the fp8
+token-group quantiser uses torch's float8_e4m3fn cast.  Only suitable for tiny shapes.
 """
 import numpy as np
 import scipy.special as sps
@@ -35,10 +35,21 @@ def fp8_group_quant_torch(x: np.ndarray) -> np.ndarray:
     return (q * s.to(torch.float64)).reshape(rows, cols).numpy()
 
 
-def dense_moe(logits, x, w1, w2, k, sigmoid=False, renorm=False, fp8_act=False):
+def gated(G, U, gelu=False):
+    """silu(G) * U, written as G * sigmoid(G) * U; or gelu(G) * U as G * Phi(G) * U
+    with scipy's normal CDF."""
+    return G * (sps.ndtr(G) if gelu else sps.expit(G)) * U
+
+
+def dense_moe(logits, x, w1, w2, k, sigmoid=False, renorm=False, fp8_act=False, gelu=False,
+              expert_map=None, weight_on_input=False, bf16_input=False):
     """out[m] = sum_j w[m,j] * expert_{id[m,j]}(x[m]) with every expert evaluated densely.
 
-    x [M, K], w1 [E, 2I, K], w2 [E, K, I] as float64 arrays (already dequantised)."""
+    x [M, K], w1 [E, 2I, K], w2 [E, K, I] as float64 arrays (already dequantised).
+    expert_map [global E]: local expert of each global one, -1 for another shard's
+    (those picks add nothing).  weight_on_input (k = 1): the input row is w * x,
+    rounded to fp32 (numpy's float32 product) and to bf16 (torch's cast) when
+    bf16_input, and the expert output is added unweighted."""
     x = np.asarray(x, np.float64)
     w1 = np.asarray(w1, np.float64)
     w2 = np.asarray(w2, np.float64)
@@ -46,19 +57,27 @@ def dense_moe(logits, x, w1, w2, k, sigmoid=False, renorm=False, fp8_act=False):
     I = N // 2
     ids = topk_select(np.asarray(logits), k)
     wts = router_weights(np.asarray(logits), ids, sigmoid, renorm)
+    M = x.shape[0]
+    if weight_on_input:
+        assert k == 1
+        p = np.float32(1.0) * wts[:, :1].astype(np.float32) * x.astype(np.float32)   # fp32 products
+        if bf16_input:
+            p = torch.from_numpy(p).to(torch.bfloat16).to(torch.float32).numpy()
+        x = p.astype(np.float64)
     if fp8_act:
         x = fp8_group_quant_torch(x.astype(np.float32))
     H = np.einsum("mc,enc->emn", x, w1)                # [E, M, 2I]
-    G, U = H[..., :I], H[..., I:]
-    A = G * sps.expit(G) * U
+    A = gated(H[..., :I], H[..., I:], gelu)
     if fp8_act:
         A = np.stack([fp8_group_quant_torch(A[e].astype(np.float32)) for e in range(E)])
     Y = np.einsum("emi,eki->emk", A, w2)               # [E, M, K]
-    M = x.shape[0]
     out = np.zeros((M, K))
     for m in range(M):
         for j in range(k):
-            out[m] += wts[m, j] * Y[ids[m, j], m]
+            e = ids[m, j] if expert_map is None else expert_map[ids[m, j]]
+            if e < 0:
+                continue
+            out[m] += (1.0 if weight_on_input else wts[m, j]) * Y[e, m]
     return out, ids, wts
 
 
@@ -69,5 +88,4 @@ def dense_mlp(x, w1, w2):
     w2 = np.asarray(w2, np.float64)
     I = w1.shape[0] // 2
     H = x @ w1.T
-    G, U = H[:, :I], H[:, I:]
-    return (G * sps.expit(G) * U) @ w2.T
+    return gated(H[:, :I], H[:, I:]) @ w2.T

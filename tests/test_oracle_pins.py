@@ -348,6 +348,125 @@ def test_combine_is_weighted_sum():
     np.testing.assert_allclose(oracle.combine(w, y), np.einsum("mj,mjk->mk", w, y), rtol=1e-13)
 
 
+# ------------------------------------------ GELU, expert-parallel shard, router weight on input
+
+def test_gelu_expert_closed_form():
+    """gelu_and_mul: with a = [1], gate rows g_j and up rows 1, act_j = gelu(g_j)
+    = g_j * Phi(g_j).  Checked against textbook values of the normal CDF,
+    scipy's ndtr and the odd-symmetry identity gelu(x) - gelu(-x) = x."""
+    g = np.array([-3.0, -2.0, -1.0, -0.5, 0.0, 0.5, 1.0, 2.0, 3.0])
+    I = g.size
+    w1 = np.concatenate([g, np.ones(I)]).reshape(1, 2 * I, 1).astype(np.float32)
+    w2 = np.ones((1, 1, I), np.float32)
+    act, _ = oracle.expert_row(np.array([1.0]), 0, w1, w2, oracle.F32, I, activation=oracle.GELU)
+    np.testing.assert_allclose(act, g * sps.ndtr(g), rtol=1e-14, atol=1e-16)
+    # Phi(1) = 0.8413447460685429, Phi(2) = 0.9772498680518208 (tables of the normal CDF)
+    np.testing.assert_allclose(act[g == 1.0], 0.8413447460685429, rtol=1e-14)
+    np.testing.assert_allclose(act[g == 2.0], 2 * 0.9772498680518208, rtol=1e-14)
+    np.testing.assert_allclose(act[g == -1.0], -(1 - 0.8413447460685429), rtol=1e-13)
+    np.testing.assert_allclose(act[g > 0] - act[g < 0][::-1], g[g > 0], rtol=1e-14)
+    assert act[g == 0.0] == 0.0
+    silu, _ = oracle.expert_row(np.array([1.0]), 0, w1, w2, oracle.F32, I)
+    np.testing.assert_allclose(silu, g * sps.expit(g), rtol=1e-14, atol=1e-16)
+
+
+@pytest.mark.parametrize("M,K,I,E,k", [(6, 8, 4, 3, 2), (9, 16, 8, 6, 3)])
+def test_gelu_layer_matches_dense_brute_force(M, K, I, E, k):
+    d = _tiny(M, K, I, E, k, seed=M * 17 + E)
+    out, _, _ = oracle.moe_tokens(_wl(M, K, I, E, k, activation=oracle.GELU), d)
+    ref, _, _ = bf.dense_moe(d["logits"], d["x"], d["w1"], d["w2"], k, gelu=True)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(oracle.dense_mlp_tokens(d["x"], d["w1"][0], d["w2"][0], I, oracle.F32,
+                                                       activation=oracle.GELU),
+                               _dense_gelu(d["x"], d["w1"][0], d["w2"][0]), rtol=1e-12, atol=1e-14)
+
+
+def _dense_gelu(x, w1, w2):
+    x, w1, w2 = (np.asarray(a, np.float64) for a in (x, w1, w2))
+    I = w1.shape[0] // 2
+    H = x @ w1.T
+    return bf.gated(H[:, :I], H[:, I:], gelu=True) @ w2.T
+
+
+def _shard(d, Eg, n_shards, s):
+    """Shard s of n: global experts g with g % n == s, local index g // n."""
+    glob = np.arange(Eg)[np.arange(Eg) % n_shards == s]
+    emap = np.full(Eg, -1, np.int32)
+    emap[glob] = np.arange(glob.size, dtype=np.int32)
+    return dict(d, w1=np.ascontiguousarray(d["w1"][glob]), w2=np.ascontiguousarray(d["w2"][glob]),
+                expert_map=emap), glob.size
+
+
+@pytest.mark.parametrize("fmt", [oracle.STANDARD, oracle.BATCHED])
+def test_expert_shards_sum_to_the_full_layer(fmt):
+    """One expert-parallel shard computes only its experts' picks; the shards'
+    outputs add up to the unsharded layer (and each matches a dense brute force
+    over its experts)."""
+    M, K, I, Eg, k = 20, 16, 8, 8, 3
+    d = _tiny(M, K, I, Eg, k, seed=21)
+    full, fids, _ = oracle.moe_tokens(_wl(M, K, I, Eg, k, format=fmt, capacity=M), d)
+    total = np.zeros_like(full)
+    for s in range(3):
+        ds, El = _shard(d, Eg, 3, s)
+        wl = _wl(M, K, I, El, k, global_E=Eg, format=fmt, capacity=M)
+        out, ids, _ = oracle.moe_tokens(wl, ds)
+        np.testing.assert_array_equal(ids, fids)                     # routing is global
+        ref, _, _ = bf.dense_moe(d["logits"], d["x"], ds["w1"], ds["w2"], k, expert_map=ds["expert_map"])
+        np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-14)
+        total += out
+    np.testing.assert_allclose(total, full, rtol=1e-12, atol=1e-14)
+
+
+def test_identity_and_empty_expert_maps():
+    M, K, I, E, k = 10, 8, 4, 5, 2
+    d = _tiny(M, K, I, E, k, seed=22)
+    base, _, _ = oracle.moe_tokens(_wl(M, K, I, E, k), d)
+    ident = dict(d, expert_map=np.arange(E, dtype=np.int32))
+    np.testing.assert_array_equal(oracle.moe_tokens(_wl(M, K, I, E, k, global_E=E), ident)[0], base)
+    none_local = dict(d, expert_map=np.full(E, -1, np.int32))
+    np.testing.assert_array_equal(oracle.moe_tokens(_wl(M, K, I, E, k, global_E=E), none_local)[0], 0.0)
+
+
+def test_count_and_permutations_skip_other_shards_pairs():
+    ids = np.array([[2, -1], [0, 2], [-1, -1], [1, 0]], np.int32)
+    np.testing.assert_array_equal(oracle.count(ids, 3), [2, 1, 2])
+    counts, offsets, perm, inv = oracle.permute_standard(ids, 3, align=2)
+    flat = ids.ravel()
+    assert np.all(inv[flat < 0] == -1)
+    np.testing.assert_array_equal(np.sort(perm[perm >= 0]), np.nonzero(flat >= 0)[0])
+    np.testing.assert_array_equal(flat[perm[perm >= 0]], np.sort(flat[flat >= 0], kind="stable"))
+    cb, invb = oracle.permute_batched(ids, 3, cap=4)
+    np.testing.assert_array_equal(cb, counts)
+    assert np.all(invb[flat < 0] == -1)
+    np.testing.assert_array_equal(invb[flat >= 0] // 4, flat[flat >= 0])
+
+
+@pytest.mark.parametrize("act_dtype", [oracle.F32, oracle.BF16])
+def test_router_weight_on_input_matches_brute_force(act_dtype):
+    """topk = 1: the expert sees w * x (held in the activation dtype) and its
+    output is added unweighted."""
+    M, K, I, E = 12, 16, 8, 4
+    d = _tiny(M, K, I, E, 1, seed=23)
+    wl = _wl(M, K, I, E, 1, router_weight_on_input=True, act_dtype=act_dtype)
+    if act_dtype == oracle.BF16:
+        xb = torch.from_numpy(d["x"]).to(torch.bfloat16)
+        d = dict(d, x=xb)
+        xin = xb.float().numpy()
+    else:
+        xin = d["x"]
+    out, _, w = oracle.moe_tokens(wl, d)
+    assert np.all(w < 1.0)
+    ref, _, _ = bf.dense_moe(d["logits"], xin, d["w1"], d["w2"], 1, weight_on_input=True,
+                             bf16_input=act_dtype == oracle.BF16)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-14)
+    # a renormalised single pick has weight 1: exactly the unweighted-input layer
+    wl1 = wl.replace(renormalize=True)
+    np.testing.assert_array_equal(oracle.moe_tokens(wl1, d)[0],
+                                  oracle.moe_tokens(wl1.replace(router_weight_on_input=False), d)[0])
+    with pytest.raises(ValueError):
+        oracle.moe_tokens(_wl(M, K, I, E, 2, router_weight_on_input=True), _tiny(M, K, I, E, 2, seed=1))
+
+
 # ------------------------------------------------------- planted mistakes
 
 # (name, text in moe_oracle.c, replacement, the pin test(s) that must catch it)
@@ -380,6 +499,21 @@ MUTANTS = [
      [lambda: test_layer_matches_dense_brute_force(9, 16, 8, 6, 3, True, True), test_combine_is_weighted_sum]),
     ("sigmoid scoring uses softmax", "double p = scoring == OR_SOFTMAX ?", "double p = 1 ?",
      [lambda: test_route_weights_match_scipy(True, False)]),
+    ("gelu in its tanh form", "0.5 * g * (1.0 + erf(g / sqrt(2.0)))",
+     "0.5 * g * (1.0 + tanh(0.7978845608028654 * (g + 0.044715 * g * g * g)))",
+     [test_gelu_expert_closed_form, lambda: test_gelu_layer_matches_dense_brute_force(6, 8, 4, 3, 2)]),
+    ("expert map ignored", "lids[f] = expert_map ? expert_map[ids[f]] : ids[f];",
+     "lids[f] = ids[f] % E;",
+     [lambda: test_expert_shards_sum_to_the_full_layer(oracle.STANDARD)]),
+    ("router weight applied twice", "wc[j] = weight_on_input ? 1.0 : wts[m * k + j];",
+     "wc[j] = wts[m * k + j];",
+     [lambda: test_router_weight_on_input_matches_brute_force(oracle.F32)]),
+    ("router weight on input ignored", "oracle_input_row(act_dtype, act_quant, x, K, m, weight_on_input,",
+     "oracle_input_row(act_dtype, act_quant, x, K, m, 0,",
+     [lambda: test_router_weight_on_input_matches_brute_force(oracle.F32)]),
+    ("weighted bf16 input not rounded to bf16", "return act_dtype == OR_BF16 ? (double)round_bf16(p) : (double)p;",
+     "return (double)p;",
+     [lambda: test_router_weight_on_input_matches_brute_force(oracle.BF16)]),
 ]
 
 

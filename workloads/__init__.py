@@ -64,6 +64,9 @@ class Workload:
     logits_dist: str = "normal"  # normal | uniform | zipf
     zipf_s: float = 1.2
     shared_I: int = 0            # >0: one always-on shared expert of this size
+    global_E: int = 0            # >0: experts in the global space (router width); E are local
+    activation: int = 0          # 0 silu_and_mul, 1 gelu_and_mul
+    router_weight_on_input: bool = False   # topk == 1 only
 
     @property
     def N(self) -> int:
@@ -117,21 +120,22 @@ def _torch_dtype(code: int):
 
 
 def make_logits(w: Workload, seed: int = 0, device="cpu") -> torch.Tensor:
-    """Router logits [M, E], fp32."""
+    """Router logits [M, router width], fp32 (the router width is global_E when set, else E)."""
     g = generator(seed, "logits", device)
+    E = w.global_E or w.E
     if w.logits_dist == "normal":
-        return torch.randn(w.M, w.E, generator=g, device=device)
+        return torch.randn(w.M, E, generator=g, device=device)
     if w.logits_dist == "uniform":
-        return torch.rand(w.M, w.E, generator=g, device=device)
+        return torch.rand(w.M, E, generator=g, device=device)
     if w.logits_dist == "zipf":
         # Gumbel noise plus log-popularity: with p_r proportional to r^-s over a
         # seeded ranking of the experts, the arg-max of each row is distributed
         # exactly as p (Gumbel-max), so expert load follows Zipf(s).
         gp = generator(seed, "zipf-rank", "cpu")
-        rank = torch.randperm(w.E, generator=gp).to(torch.float64) + 1.0
+        rank = torch.randperm(E, generator=gp).to(torch.float64) + 1.0
         p = rank ** (-w.zipf_s)
         logp = torch.log(p / p.sum()).to(torch.float32).to(device)
-        u = torch.rand(w.M, w.E, generator=g, device=device)
+        u = torch.rand(w.M, E, generator=g, device=device)
         u = u.clamp_min(torch.finfo(torch.float32).tiny)
         gumbel = -torch.log(-torch.log(u))
         return (gumbel + logp[None, :]).contiguous()
