@@ -24,6 +24,7 @@ FORMAT_STANDARD, FORMAT_BATCHED_EXPERTS = 0, 1
 DTYPE_F32, DTYPE_BF16, DTYPE_FP8_E4M3 = 0, 1, 2
 QUANT_NONE, QUANT_FP8_TOKEN_GROUP_128 = 0, 1
 SCORING_SOFTMAX, SCORING_SIGMOID = 0, 1
+ACTIVATION_SILU, ACTIVATION_GELU = 0, 1
 DEVICE_BAD_EXPERT_ID, DEVICE_CAPACITY_OVERFLOW = 1, 2
 WEIGHTS_ROW_MAJOR, WEIGHTS_PACKED = 0, 1
 NUM_STAGE_EVENTS = 6
@@ -39,7 +40,7 @@ class Problem(C.Structure):
     _fields_ = [
         ("E", C.c_int64), ("M", C.c_int64), ("N", C.c_int64), ("K", C.c_int64),
         ("topk", C.c_int64), ("max_tokens_per_expert", C.c_int64), ("align", C.c_int64),
-        ("shared_N", C.c_int64),
+        ("shared_N", C.c_int64), ("global_E", C.c_int64),
         ("format", C.c_int32), ("act_dtype", C.c_int32), ("w_dtype", C.c_int32),
         ("act_quant", C.c_int32), ("scoring", C.c_int32), ("renormalize", C.c_int32),
         ("activation", C.c_int32), ("apply_router_weight_on_input", C.c_int32),
@@ -91,7 +92,7 @@ def load_library(path: str = LIB_PATH):
         "moe_workspace_layout": [P(Problem), P(WsLayout)],
         "moe_pack_weights": [P(Problem), P(Weights), vp, vp, vp],
         "moe_route": [P(Problem), vp, vp, vp, vp],
-        "moe_prepare": [P(Problem), vp, vp, vp, vp, vp, vp, C.c_size_t, vp],
+        "moe_prepare": [P(Problem), vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp],
         "moe_experts": [P(Problem), vp, vp, P(Weights), vp, vp, vp, C.c_size_t, vp],
         "moe_finalize": [P(Problem), vp, vp, vp, vp, C.c_size_t, vp],
         "moe_shared_expert": [P(Problem), vp, vp, vp, vp, vp, C.c_size_t, vp],
@@ -134,11 +135,18 @@ def _ws(ws: torch.Tensor):
 
 def make_problem(E, M, N, K, topk, *, format=FORMAT_STANDARD, act_dtype=DTYPE_BF16, w_dtype=DTYPE_BF16,
                  act_quant=QUANT_NONE, scoring=SCORING_SOFTMAX, renormalize=False,
-                 max_tokens_per_expert=0, align=0, shared_N=0, weight_layout=WEIGHTS_ROW_MAJOR) -> Problem:
+                 max_tokens_per_expert=0, align=0, shared_N=0, weight_layout=WEIGHTS_ROW_MAJOR,
+                 activation=ACTIVATION_SILU, apply_router_weight_on_input=False, global_E=0,
+                 expert_map: Optional[torch.Tensor] = None) -> Problem:
+    """expert_map: device int32 tensor [global_E] (local expert or -1); the
+    caller keeps it alive while the problem is in use."""
+    if expert_map is not None and (expert_map.dtype != torch.int32 or expert_map.numel() != (global_E or E)):
+        raise ValueError("expert_map must be an int32 tensor of global_E entries")
     return Problem(E=E, M=M, N=N, K=K, topk=topk, max_tokens_per_expert=max_tokens_per_expert, align=align,
-                   shared_N=shared_N, format=format, act_dtype=act_dtype, w_dtype=w_dtype,
-                   act_quant=act_quant, scoring=scoring, renormalize=int(renormalize), activation=0,
-                   apply_router_weight_on_input=0, weight_layout=weight_layout, reserved=0, expert_map=None)
+                   shared_N=shared_N, global_E=global_E, format=format, act_dtype=act_dtype, w_dtype=w_dtype,
+                   act_quant=act_quant, scoring=scoring, renormalize=int(renormalize), activation=activation,
+                   apply_router_weight_on_input=int(apply_router_weight_on_input), weight_layout=weight_layout,
+                   reserved=0, expert_map=_ptr(expert_map))
 
 
 def validate(p: Problem) -> int:
@@ -180,10 +188,13 @@ def moe_route(p: Problem, logits, topk_weights, topk_ids, stream=None):
                                     _stream(stream)), "moe_route")
 
 
-def moe_prepare(p: Problem, x, topk_ids, a_out, a_scale_out, expert_num_tokens, workspace, stream=None):
+def moe_prepare(p: Problem, x, topk_ids, a_out, a_scale_out, expert_num_tokens, workspace, stream=None,
+                topk_weights=None):
+    """topk_weights is read only with apply_router_weight_on_input."""
     wp, wn = _ws(workspace)
-    _check(load_library().moe_prepare(C.byref(p), _ptr(x), _ptr(topk_ids), _ptr(a_out), _ptr(a_scale_out),
-                                      _ptr(expert_num_tokens), wp, wn, _stream(stream)), "moe_prepare")
+    _check(load_library().moe_prepare(C.byref(p), _ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(a_out),
+                                      _ptr(a_scale_out), _ptr(expert_num_tokens), wp, wn, _stream(stream)),
+           "moe_prepare")
 
 
 def _weights(w1, w1_scale, w2, w2_scale) -> Weights:

@@ -5,7 +5,9 @@
 // the (M, K) output, which it overwrites; on one GPU there is no combine
 // communication, only this gather-weight-reduce.  Rows come from
 // fused_out[m*topk + j] (Standard) or from the batched row the dispatch placed
-// pair (m, j) in (BatchedExperts); a dropped pair adds nothing.
+// pair (m, j) in (BatchedExperts); a dropped pair, or the pick of an expert
+// another expert-parallel shard holds, adds nothing.  With the router weight
+// applied on the input the outputs are added unweighted.
 //
 // HBM-bound: one block per token, 16-byte vector loads of each of the k rows,
 // fp32 accumulation in j order, one 16-byte store per 8 outputs.
@@ -16,16 +18,17 @@ namespace {
 
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ y, const float *__restrict__ w,
-                                                      const int32_t *__restrict__ inv, int K, int k,
-                                                      T *__restrict__ out) {
+                                                      const int32_t *__restrict__ inv, int rows_from_inv,
+                                                      int K, int k, T *__restrict__ out) {
   const int m = blockIdx.x;
   for (int c = threadIdx.x * 8; c < K; c += 256 * 8) {
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int j = 0; j < k; ++j) {
       const int64_t pair = (int64_t)m * k + j;
-      const int64_t row = inv ? (int64_t)inv[pair] : pair;
-      if (row < 0) continue;
-      const float wj = w[pair];
+      const int64_t slot = inv ? (int64_t)inv[pair] : pair;
+      if (slot < 0) continue;                      // dropped, or another shard's pick
+      const int64_t row = rows_from_inv ? slot : pair;
+      const float wj = w ? w[pair] : 1.0f;
       if constexpr (sizeof(T) == 2) {
         const uint4 raw = *reinterpret_cast<const uint4 *>(y + row * K + c);
         const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
@@ -58,14 +61,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ y, c
 }  // namespace
 
 hipError_t launch_combine(const moe_problem &p, const void *fused_out, const float *topk_w,
-                          const int32_t *inv, void *out, hipStream_t s) {
+                          const int32_t *inv, bool rows_from_inv, void *out, hipStream_t s) {
   dim3 grid((unsigned)p.M), block(256);
-  const int K = (int)p.K, k = (int)p.topk;
+  const int K = (int)p.K, k = (int)p.topk, r = rows_from_inv ? 1 : 0;
   if (p.act_dtype == MOE_DTYPE_BF16)
-    combine_kernel<uint16_t><<<grid, block, 0, s>>>((const uint16_t *)fused_out, topk_w, inv, K, k,
+    combine_kernel<uint16_t><<<grid, block, 0, s>>>((const uint16_t *)fused_out, topk_w, inv, r, K, k,
                                                     (uint16_t *)out);
   else
-    combine_kernel<float><<<grid, block, 0, s>>>((const float *)fused_out, topk_w, inv, K, k, (float *)out);
+    combine_kernel<float><<<grid, block, 0, s>>>((const float *)fused_out, topk_w, inv, r, K, k, (float *)out);
   return hipGetLastError();
 }
 

@@ -25,16 +25,16 @@ constexpr int kMaxExperts = 1024;
 // ----------------------------------------------------------- histogram
 
 __global__ __launch_bounds__(256) void chunk_hist_kernel(const int32_t *__restrict__ ids, int n,
-                                                         int E, int chunk,
-                                                         int32_t *__restrict__ chunk_hist) {
+                                                         int E, int Eg, const int32_t *__restrict__ map,
+                                                         int chunk, int32_t *__restrict__ chunk_hist) {
   __shared__ int h[kMaxExperts];
   for (int e = threadIdx.x; e < E; e += blockDim.x) h[e] = 0;
   __syncthreads();
   const int c = blockIdx.x;
   const int f0 = c * chunk, f1 = min(n, f0 + chunk);
   for (int f = f0 + threadIdx.x; f < f1; f += blockDim.x) {
-    int e = ids[f];
-    if (e >= 0 && e < E) atomicAdd(&h[e], 1);
+    const int e = local_expert(ids[f], Eg, map, E);
+    if (e >= 0) atomicAdd(&h[e], 1);
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) chunk_hist[(int64_t)c * E + e] = h[e];
@@ -106,6 +106,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t *__restrict__ chunk_
 
 // One wavefront per chunk: stable rank of each pair inside its expert.
 __global__ __launch_bounds__(64) void rank_kernel(const int32_t *__restrict__ ids, int n, int E,
+                                                  int Eg, const int32_t *__restrict__ map,
                                                   int nbits, int chunk, int standard, int64_t cap,
                                                   const int32_t *__restrict__ chunk_prefix,
                                                   const int32_t *__restrict__ offsets,
@@ -121,11 +122,11 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t *__restrict__ id
   for (int base = f0; base < f1; base += 64) {
     const int f = base + lane;
     const bool valid = f < f1;
-    const int e = valid ? ids[f] : -1;
-    const bool good = valid && e >= 0 && e < E;
+    const int e = valid ? local_expert(ids[f], Eg, map, E) : -1;
+    const bool good = valid && e >= 0;
     if (valid && !good) {
-      inv[f] = -1;
-      atomicOr(status, MOE_DEVICE_BAD_EXPERT_ID);
+      inv[f] = -1;                                   // another shard's pick, or invalid
+      if (e == -2) atomicOr(status, MOE_DEVICE_BAD_EXPERT_ID);
     }
     uint64_t peers = __ballot(good);
     for (int b = 0; b < nbits; ++b) {
@@ -159,9 +160,12 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t *__restrict__ id
 // team, scale, codes.  Each row is read once and written to every destination
 // row: the rows inv[] names for its topk pairs (batched), or row m (standard
 // quantise).
+// With topk_w (router weight on the input, topk == 1) the row is first
+// multiplied by the token's weight and rounded to the activation type.
 template <typename TIn, bool QUANT>
 __global__ __launch_bounds__(256) void dispatch_rows_kernel(const TIn *__restrict__ x, int K, int k,
                                                             const int32_t *__restrict__ inv,
+                                                            const float *__restrict__ topk_w,
                                                             void *__restrict__ a_out,
                                                             float *__restrict__ a_scale) {
   const int m = blockIdx.x;
@@ -182,6 +186,14 @@ __global__ __launch_bounds__(256) void dispatch_rows_kernel(const TIn *__restric
       const float4 *src = reinterpret_cast<const float4 *>(x + (int64_t)m * K + c0);
       float4 a = src[0], b = src[1];
       v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
+    }
+    if (topk_w) {
+      const float wm = topk_w[m];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        v[i] *= wm;
+        if constexpr (sizeof(TIn) == 2) v[i] = bf16_bits_to_f32(f32_to_bf16_bits(v[i]));
+      }
     }
     if constexpr (QUANT) {
       float amax = 0.0f;
@@ -207,8 +219,11 @@ __global__ __launch_bounds__(256) void dispatch_rows_kernel(const TIn *__restric
         const int64_t d = inv ? inv[(int64_t)m * k + j] : m;
         if (d < 0) continue;
         if constexpr (sizeof(TIn) == 2) {
-          *reinterpret_cast<uint4 *>(reinterpret_cast<TIn *>(a_out) + d * K + c0) =
-              *reinterpret_cast<const uint4 *>(x + (int64_t)m * K + c0);
+          uint32_t u[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            u[i] = (uint32_t)f32_to_bf16_bits(v[2 * i]) | ((uint32_t)f32_to_bf16_bits(v[2 * i + 1]) << 16);
+          *reinterpret_cast<uint4 *>(reinterpret_cast<TIn *>(a_out) + d * K + c0) = make_uint4(u[0], u[1], u[2], u[3]);
         } else {
           float4 *dst = reinterpret_cast<float4 *>(reinterpret_cast<TIn *>(a_out) + d * K + c0);
           dst[0] = make_float4(v[0], v[1], v[2], v[3]);
@@ -318,38 +333,39 @@ int ceil_log2(int v) {
 hipError_t launch_count_and_permute(const moe_problem &p, const int32_t *ids,
                                     int32_t *expert_num_tokens, const DispatchBufs &b,
                                     hipStream_t s) {
-  const int n = (int)(p.M * p.topk), E = (int)p.E;
+  const int n = (int)(p.M * p.topk), E = (int)p.E, Eg = (int)router_width(p);
   const int standard = p.format == MOE_FORMAT_STANDARD;
   const int align = p.align > 0 ? (int)p.align : 1;
-  chunk_hist_kernel<<<(unsigned)b.n_chunks, 256, 0, s>>>(ids, n, E, (int)b.chunk, b.chunk_hist);
+  chunk_hist_kernel<<<(unsigned)b.n_chunks, 256, 0, s>>>(ids, n, E, Eg, p.expert_map, (int)b.chunk,
+                                                          b.chunk_hist);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   scan_kernel<<<1, 1024, 0, s>>>(b.chunk_hist, (int)b.n_chunks, E, align, standard, b.counts,
                                  expert_num_tokens, b.offsets, b.perm, b.perm_len, b.status);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  rank_kernel<<<(unsigned)b.n_chunks, 64, 0, s>>>(ids, n, E, ceil_log2(E), (int)b.chunk, standard,
+  rank_kernel<<<(unsigned)b.n_chunks, 64, 0, s>>>(ids, n, E, Eg, p.expert_map, ceil_log2(E), (int)b.chunk, standard,
                                                   p.max_tokens_per_expert, b.chunk_hist, b.offsets,
                                                   b.perm, b.inv, b.status);
   return hipGetLastError();
 }
 
-hipError_t launch_dispatch_rows(const moe_problem &p, const void *x, const int32_t *inv, void *a_out,
-                                float *a_scale_out, bool batched, hipStream_t s) {
+hipError_t launch_dispatch_rows(const moe_problem &p, const void *x, const int32_t *inv, const float *topk_w,
+                                void *a_out, float *a_scale_out, bool batched, hipStream_t s) {
   const int K = (int)p.K, k = (int)p.topk;
   const bool quant = p.act_quant == MOE_QUANT_FP8_TOKEN_GROUP_128;
   const int32_t *d = batched ? inv : nullptr;
   dim3 grid((unsigned)p.M), block(256);
   if (p.act_dtype == MOE_DTYPE_BF16) {
     if (quant)
-      dispatch_rows_kernel<uint16_t, true><<<grid, block, 0, s>>>((const uint16_t *)x, K, k, d, a_out, a_scale_out);
+      dispatch_rows_kernel<uint16_t, true><<<grid, block, 0, s>>>((const uint16_t *)x, K, k, d, topk_w, a_out, a_scale_out);
     else
-      dispatch_rows_kernel<uint16_t, false><<<grid, block, 0, s>>>((const uint16_t *)x, K, k, d, a_out, a_scale_out);
+      dispatch_rows_kernel<uint16_t, false><<<grid, block, 0, s>>>((const uint16_t *)x, K, k, d, topk_w, a_out, a_scale_out);
   } else {
     if (quant)
-      dispatch_rows_kernel<float, true><<<grid, block, 0, s>>>((const float *)x, K, k, d, a_out, a_scale_out);
+      dispatch_rows_kernel<float, true><<<grid, block, 0, s>>>((const float *)x, K, k, d, topk_w, a_out, a_scale_out);
     else
-      dispatch_rows_kernel<float, false><<<grid, block, 0, s>>>((const float *)x, K, k, d, a_out, a_scale_out);
+      dispatch_rows_kernel<float, false><<<grid, block, 0, s>>>((const float *)x, K, k, d, topk_w, a_out, a_scale_out);
   }
   return hipGetLastError();
 }

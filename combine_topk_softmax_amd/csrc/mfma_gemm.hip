@@ -217,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const GemmParams g,
       const int64_t slot = row0 + r;
       if constexpr (GATED) {
         const float gt = acc[mb][0][i], up = acc[mb][1][i];
-        const float v = gt / (1.0f + expf(-gt)) * up;
+        const float v = gated_act(gt, up, g.act);
         const int64_t col = (int64_t)nt * 128 + wn * 32 + (lane & 31);
         reinterpret_cast<uint16_t *>(g.out)[slot * g.ldo + col] = f32_to_bf16_bits(v);
       } else {

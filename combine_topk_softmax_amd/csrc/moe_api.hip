@@ -32,7 +32,10 @@ moe_status validate(const moe_problem *pp) {
   if (!pp) return MOE_ERR_INVALID_ARG;
   const moe_problem &p = *pp;
   if (p.E < 1 || p.M < 0 || p.N < 2 || p.K < 1 || p.topk < 1) return MOE_ERR_INVALID_ARG;
-  if (p.N % 2 != 0 || p.topk > p.E) return MOE_ERR_INVALID_ARG;
+  if (p.global_E < 0) return MOE_ERR_INVALID_ARG;
+  const int64_t Eg = router_width(p);
+  if (p.N % 2 != 0 || p.topk > Eg || p.E > Eg) return MOE_ERR_INVALID_ARG;
+  if (!p.expert_map && Eg != p.E) return MOE_ERR_INVALID_ARG;   // no map: global == local
   if (p.format != MOE_FORMAT_STANDARD && p.format != MOE_FORMAT_BATCHED_EXPERTS) return MOE_ERR_INVALID_ARG;
   if (p.scoring != MOE_SCORING_SOFTMAX && p.scoring != MOE_SCORING_SIGMOID) return MOE_ERR_INVALID_ARG;
   if (p.align < 0 || p.shared_N < 0) return MOE_ERR_INVALID_ARG;
@@ -41,11 +44,12 @@ moe_status validate(const moe_problem *pp) {
   if (p.w_dtype != MOE_DTYPE_F32 && p.w_dtype != MOE_DTYPE_BF16 && p.w_dtype != MOE_DTYPE_FP8_E4M3)
     return MOE_ERR_INVALID_ARG;
   if (p.act_quant != MOE_QUANT_NONE && p.act_quant != MOE_QUANT_FP8_TOKEN_GROUP_128) return MOE_ERR_INVALID_ARG;
-  if (p.activation != MOE_ACTIVATION_SILU) return MOE_ERR_UNSUPPORTED;
-  if (p.apply_router_weight_on_input != 0 || p.expert_map != nullptr) return MOE_ERR_UNSUPPORTED;
+  if (p.activation != MOE_ACTIVATION_SILU && p.activation != MOE_ACTIVATION_GELU) return MOE_ERR_UNSUPPORTED;
+  if (p.apply_router_weight_on_input != 0 && p.apply_router_weight_on_input != 1) return MOE_ERR_INVALID_ARG;
+  if (p.apply_router_weight_on_input && p.topk != 1) return MOE_ERR_INVALID_ARG;   // topk == 1 only
   if (p.reserved != 0) return MOE_ERR_INVALID_ARG;
   if (p.weight_layout != MOE_WEIGHTS_ROW_MAJOR && p.weight_layout != MOE_WEIGHTS_PACKED) return MOE_ERR_INVALID_ARG;
-  if (p.E > kMaxExperts || p.topk > 64) return MOE_ERR_UNSUPPORTED;
+  if (Eg > kMaxExperts || p.topk > 64) return MOE_ERR_UNSUPPORTED;
   const int64_t I = p.N / 2;
   if (p.K % 128 != 0 || I % 64 != 0) return MOE_ERR_UNSUPPORTED;
   // dtype combinations: fp32 x fp32, bf16 x bf16, fp8-quantised x fp8
@@ -102,7 +106,7 @@ void layout(const moe_problem &p, moe_ws_layout &L) {
   L.topk_weights = take(4 * n);
   L.topk_ids = take(4 * n);
   const int64_t a_rows = standard ? p.M : E * cap;
-  const bool need_a = !standard || fp8;
+  const bool need_a = !standard || fp8 || p.apply_router_weight_on_input;
   L.a_q = take(need_a ? a_rows * p.K * (fp8 ? 1 : eb) : 0);
   L.a_scale = take(need_a && fp8 ? a_rows * (p.K / 128) * 4 : 0);
   L.fused_out = take((standard ? n : E * cap) * p.K * eb);
@@ -131,8 +135,15 @@ void record(const moe_stage_events *ev, int i, hipStream_t s) {
   if (ev && ev->ev[i]) (void)hipEventRecord(ev->ev[i], s);
 }
 
-moe_status do_prepare(const moe_problem &p, const void *x, const int32_t *ids, void *a_out,
-                      float *a_scale_out, int32_t *expert_num_tokens, void *ws,
+// Whether prepare writes the activations the experts read (a_out), rather
+// than the experts reading x directly.
+bool prepared_rows(const moe_problem &p) {
+  return p.format == MOE_FORMAT_BATCHED_EXPERTS || p.act_quant == MOE_QUANT_FP8_TOKEN_GROUP_128 ||
+         p.apply_router_weight_on_input;
+}
+
+moe_status do_prepare(const moe_problem &p, const void *x, const int32_t *ids, const float *topk_w,
+                      void *a_out, float *a_scale_out, int32_t *expert_num_tokens, void *ws,
                       const moe_ws_layout &L, hipStream_t s) {
   DispatchBufs b;
   b.status = at<int32_t>(ws, L.status);
@@ -146,8 +157,9 @@ moe_status do_prepare(const moe_problem &p, const void *x, const int32_t *ids, v
   b.chunk = L.chunk;
   MOE_HIP(launch_count_and_permute(p, ids, expert_num_tokens, b, s));
   const bool batched = p.format == MOE_FORMAT_BATCHED_EXPERTS;
-  if (batched || p.act_quant == MOE_QUANT_FP8_TOKEN_GROUP_128)
-    MOE_HIP(launch_dispatch_rows(p, x, b.inv, a_out, a_scale_out, batched, s));
+  if (prepared_rows(p))
+    MOE_HIP(launch_dispatch_rows(p, x, b.inv, p.apply_router_weight_on_input ? topk_w : nullptr, a_out,
+                                 a_scale_out, batched, s));
   return MOE_OK;
 }
 
@@ -191,6 +203,7 @@ moe_status do_experts(const moe_problem &p, const void *a, const float *a_scale,
   g1.out = at<void>(ws, L.act);
   g1.ldo = I;
   g1.half_n = I;
+  g1.act = p.activation;
   g1.w_packed = p.weight_layout == MOE_WEIGHTS_PACKED;
   g1.t = gt;
   if (streaming && fp8) {
@@ -258,6 +271,7 @@ moe_status do_shared(const moe_problem &p, const void *x, const void *w1, const 
   g1.out = at<void>(ws, L.shared_act);
   g1.ldo = Is;
   g1.half_n = Is;
+  g1.act = p.activation;
   g1.t = gt;
   const bool big = mfma_gemm_fits(p.act_dtype, p.act_dtype, p.K, Is);
   if (big)
@@ -297,7 +311,7 @@ const char *moe_status_str(moe_status s) {
   return "unknown status";
 }
 
-int moe_version(void) { return 1; }
+int moe_version(void) { return 2; }
 
 moe_status moe_validate(const moe_problem *p) { return validate(p); }
 
@@ -342,9 +356,10 @@ moe_status moe_route(const moe_problem *p, const float *logits, float *topk_weig
   return MOE_OK;
 }
 
-moe_status moe_prepare(const moe_problem *p, const void *x, const int32_t *topk_ids, void *a_out,
-                       float *a_scale_out, int32_t *expert_num_tokens, void *workspace,
-                       size_t workspace_bytes, hipStream_t stream) {
+moe_status moe_prepare(const moe_problem *p, const void *x, const int32_t *topk_ids,
+                       const float *topk_weights, void *a_out, float *a_scale_out,
+                       int32_t *expert_num_tokens, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
   moe_status st = validate(p);
   if (st != MOE_OK) return st;
   if (p->M == 0) return MOE_OK;
@@ -352,11 +367,13 @@ moe_status moe_prepare(const moe_problem *p, const void *x, const int32_t *topk_
   if ((st = check_ws(*p, workspace, workspace_bytes, L)) != MOE_OK) return st;
   if (!x || !topk_ids || !expert_num_tokens) return MOE_ERR_INVALID_ARG;
   const bool quant = p->act_quant == MOE_QUANT_FP8_TOKEN_GROUP_128;
-  const bool batched = p->format == MOE_FORMAT_BATCHED_EXPERTS;
-  if ((batched || quant) && !a_out) return MOE_ERR_INVALID_ARG;
+  const bool rows = prepared_rows(*p);
+  if (rows && !a_out) return MOE_ERR_INVALID_ARG;
   if (quant && !a_scale_out) return MOE_ERR_INVALID_ARG;
-  if (!batched && !quant && (a_out || a_scale_out)) return MOE_ERR_INVALID_ARG;
-  return do_prepare(*p, x, topk_ids, a_out, a_scale_out, expert_num_tokens, workspace, L, stream);
+  if (!rows && (a_out || a_scale_out)) return MOE_ERR_INVALID_ARG;
+  if (p->apply_router_weight_on_input && !topk_weights) return MOE_ERR_INVALID_ARG;
+  return do_prepare(*p, x, topk_ids, topk_weights, a_out, a_scale_out, expert_num_tokens, workspace, L,
+                    stream);
 }
 
 moe_status moe_experts(const moe_problem *p, const void *a, const float *a_scale,
@@ -379,9 +396,11 @@ moe_status moe_finalize(const moe_problem *p, const void *fused_out, const float
   if (p->M == 0) return MOE_OK;
   moe_ws_layout L;
   if ((st = check_ws(*p, workspace, workspace_bytes, L)) != MOE_OK) return st;
-  if (!fused_out || !topk_weights || !out) return MOE_ERR_INVALID_ARG;
-  const int32_t *inv = p->format == MOE_FORMAT_BATCHED_EXPERTS ? at<int32_t>(workspace, L.inv) : nullptr;
-  MOE_HIP(launch_combine(*p, fused_out, topk_weights, inv, out, stream));
+  if (!fused_out || !out || (!topk_weights && !p->apply_router_weight_on_input)) return MOE_ERR_INVALID_ARG;
+  const bool batched = p->format == MOE_FORMAT_BATCHED_EXPERTS;
+  const int32_t *inv = batched || p->expert_map ? at<int32_t>(workspace, L.inv) : nullptr;
+  MOE_HIP(launch_combine(*p, fused_out, p->apply_router_weight_on_input ? nullptr : topk_weights, inv, batched,
+                         out, stream));
   return MOE_OK;
 }
 
@@ -432,16 +451,17 @@ moe_status moe_forward(const moe_problem *p, const float *logits, const void *x,
 
   const bool standard = p->format == MOE_FORMAT_STANDARD;
   const bool quant = p->act_quant == MOE_QUANT_FP8_TOKEN_GROUP_128;
-  void *a_q = (!standard || quant) ? at<void>(workspace, L.a_q) : nullptr;
+  void *a_q = prepared_rows(*p) ? at<void>(workspace, L.a_q) : nullptr;
   float *a_s = quant ? at<float>(workspace, L.a_scale) : nullptr;
   int32_t *counts = at<int32_t>(workspace, L.counts);
-  if ((st = do_prepare(*p, x, ti, a_q, a_s, counts, workspace, L, stream)) != MOE_OK) return st;
+  if ((st = do_prepare(*p, x, ti, tw, a_q, a_s, counts, workspace, L, stream)) != MOE_OK) return st;
 
   void *fused = at<void>(workspace, L.fused_out);
   if ((st = do_experts(*p, a_q ? a_q : x, a_s, *w, counts, fused, workspace, L, stream, events)) != MOE_OK)
     return st;
-  const int32_t *inv = standard ? nullptr : at<int32_t>(workspace, L.inv);
-  MOE_HIP(launch_combine(*p, fused, tw, inv, out, stream));
+  // the permutation prepare just wrote masks dropped / other shards' pairs
+  MOE_HIP(launch_combine(*p, fused, p->apply_router_weight_on_input ? nullptr : tw,
+                         at<int32_t>(workspace, L.inv), !standard, out, stream));
   record(events, 5, stream);
   if (shared) MOE_HIP(hipStreamWaitEvent(stream, shared->output_ready, 0));
   return MOE_OK;

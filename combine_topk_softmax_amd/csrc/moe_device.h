@@ -56,6 +56,28 @@ __device__ __forceinline__ uint32_t quant_e4m3(float x, float scale) {
   return f32_to_e4m3(t);
 }
 
+// ------------------------------------------------------------ activation
+
+// act(gate) * up of the gated GEMM epilogues: silu_and_mul, or gelu_and_mul
+// with the exact GELU g * Phi(g) = 0.5 g (1 + erf(g / sqrt 2)).
+__device__ __forceinline__ float gated_act(float g, float u, int act) {
+  if (act == MOE_ACTIVATION_GELU) return 0.5f * g * (1.0f + erff(g * 0.70710678118654752f)) * u;
+  return g / (1.0f + expf(-g)) * u;
+}
+
+// ------------------------------------------------------- expert-parallel shard
+
+// Router width: the global experts of an expert-parallel shard, else E.
+inline int64_t router_width(const moe_problem &p) { return p.global_E > 0 ? p.global_E : p.E; }
+
+// Local expert of a routed (global) id: >= 0 local, -1 held by another shard,
+// -2 invalid (id outside [0, Eg) or a map entry outside [-1, E)).
+__device__ __forceinline__ int local_expert(int id, int Eg, const int32_t *map, int E) {
+  if (id < 0 || id >= Eg) return -2;
+  const int l = map ? map[id] : id;
+  return l == -1 ? -1 : (l >= 0 && l < E ? l : -2);
+}
+
 // ------------------------------------------------------------- wave utils
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
@@ -161,6 +183,7 @@ struct GemmParams {
   float *out_scale;           // gated fp8 streaming GEMM: if set, act is written as e4m3 codes
                               // (out, ldo bytes per row) with one scale per row and 128 columns
   int64_t half_n;             // gated: I (up rows start here)
+  int act;                    // gated: MOE_ACTIVATION_*
   int w_packed;               // weights in MOE_WEIGHTS_PACKED order
   GemmTiles t;
 };
@@ -175,8 +198,10 @@ struct DispatchBufs {
 
 hipError_t launch_count_and_permute(const moe_problem &p, const int32_t *ids, int32_t *expert_num_tokens,
                                     const DispatchBufs &b, hipStream_t s);
-hipError_t launch_dispatch_rows(const moe_problem &p, const void *x, const int32_t *inv, void *a_out,
-                                float *a_scale_out, bool batched, hipStream_t s);
+// Row quantise / scatter; topk_w non-NULL applies each token's (single)
+// router weight to its input row first (apply_router_weight_on_input).
+hipError_t launch_dispatch_rows(const moe_problem &p, const void *x, const int32_t *inv, const float *topk_w,
+                                void *a_out, float *a_scale_out, bool batched, hipStream_t s);
 hipError_t launch_plan_tiles(const moe_problem &p, const int32_t *counts, const int32_t *offsets,
                              int64_t perm_len, int tile_rows, int max_tiles, int32_t *tiles,
                              int32_t *status, hipStream_t s);
@@ -201,8 +226,11 @@ int mfma_gemm_n_tiles(GemmKind kind, int64_t Nw);
 hipError_t launch_mfma_gemm(GemmKind kind, const GemmParams &g, int n_tiles, hipStream_t s);
 hipError_t launch_pack_weights(const void *src, void *dst, int64_t E, int64_t Nw, int64_t row_bytes, bool gated,
                                hipStream_t s);
+// Combine.  Rows: inv[pair] with rows_from_inv (batched), else pair; with
+// inv non-NULL a pair whose inv is negative adds nothing.  topk_w NULL: the
+// outputs are added unweighted (router weight applied on the input).
 hipError_t launch_combine(const moe_problem &p, const void *fused_out, const float *topk_w,
-                          const int32_t *inv, void *out, hipStream_t s);
+                          const int32_t *inv, bool rows_from_inv, void *out, hipStream_t s);
 
 constexpr int kTileRows = 128;   // grouped-GEMM rows per tile (BM)
 constexpr int kTileCols = 128;   // grouped-GEMM weight rows per tile (BN)

@@ -93,7 +93,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float *__restrict__ lo
 
 hipError_t launch_route(const moe_problem &p, const float *logits, float *w, int32_t *ids,
                         hipStream_t s) {
-  const int M = (int)p.M, E = (int)p.E, k = (int)p.topk;
+  const int M = (int)p.M, E = (int)router_width(p), k = (int)p.topk;
   dim3 grid((M + 3) / 4), block(256);
   const int sig = p.scoring == MOE_SCORING_SIGMOID, ren = p.renormalize != 0;
   if (E <= 64)

@@ -199,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float gt = acc[mb][0][i], up = acc[mb][1][i];
-        v[mb][i] = gt / (1.0f + expf(-gt)) * up;
+        v[mb][i] = gated_act(gt, up, g.act);
         float m = fabsf(v[mb][i]);
 #pragma unroll
         for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
         const int64_t slot = row0 + r;
         if constexpr (GATED) {
           const float gt = acc[mb][0][i], up = acc[mb][1][i];
-          const float v = gt / (1.0f + expf(-gt)) * up;
+          const float v = gated_act(gt, up, g.act);
           const int64_t col = (int64_t)nt * 128 + wv * 16 + r16;
           if constexpr (OUT_BF16)
             reinterpret_cast<uint16_t *>(g.out)[slot * g.ldo + col] = f32_to_bf16_bits(v);

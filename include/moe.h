@@ -62,7 +62,10 @@ enum { MOE_FORMAT_STANDARD = 0, MOE_FORMAT_BATCHED_EXPERTS = 1 };
 enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1, MOE_DTYPE_FP8_E4M3 = 2 };
 enum { MOE_QUANT_NONE = 0, MOE_QUANT_FP8_TOKEN_GROUP_128 = 1 };
 enum { MOE_SCORING_SOFTMAX = 0, MOE_SCORING_SIGMOID = 1 };
-enum { MOE_ACTIVATION_SILU = 0 };
+/* FusedMoEPermuteExpertsUnpermute.activation (modular_kernel.py page):
+ * silu_and_mul, or gelu_and_mul with the exact GELU g * Phi(g)
+ * = 0.5 g (1 + erf(g / sqrt 2)). */
+enum { MOE_ACTIVATION_SILU = 0, MOE_ACTIVATION_GELU = 1 };
 
 /* Weight layouts.  ROW_MAJOR is w1 [E, N, K] / w2 [E, K, N/2] as above.
  * PACKED is the same bytes reordered by moe_pack_weights so that each
@@ -79,7 +82,21 @@ enum { MOE_DEVICE_BAD_EXPERT_ID = 1, MOE_DEVICE_CAPACITY_OVERFLOW = 2 };
  * N = 2*I: w1 holds the gate rows [0, I) then the up rows [I, 2I) (the page
  * fixes only that the activation halves the width).
  * Unlike the page's 3-D case, M always counts tokens; the batched capacity
- * is max_tokens_per_expert. */
+ * is max_tokens_per_expert.
+ *
+ * Expert-parallel shard (the page's expert_map / global_num_experts /
+ * local_num_experts): E counts this GPU's local experts (weights, counts);
+ * the router picks among global_E experts (logits [M, global_E], topk_ids in
+ * [0, global_E)); expert_map (device int32[global_E]) gives each global expert
+ * its local index or -1 when another shard holds it.  Picks of other shards
+ * are neither counted nor computed and add nothing to this call's output, so
+ * the shards' outputs sum to the unsharded layer's.  expert_map NULL and
+ * global_E 0 (or E) is the plain one-shard layer.
+ *
+ * apply_router_weight_on_input (topk == 1 only; FusedMoEModularKernel.forward
+ * on the page): prepare multiplies each token's input row by its router
+ * weight, rounded to act_dtype, before any quantisation, and the combine adds
+ * the expert output unweighted. */
 typedef struct moe_problem {
   int64_t E;
   int64_t M;
@@ -89,17 +106,18 @@ typedef struct moe_problem {
   int64_t max_tokens_per_expert; /* BATCHED_EXPERTS: rows per expert buffer  */
   int64_t align;                 /* STANDARD: pad expert segments to this (0 = 1) */
   int64_t shared_N;              /* rows of the shared expert's w1 (2*I_s); 0 = none */
+  int64_t global_E;              /* router width (experts in the global space); 0 = E */
   int32_t format;                /* MOE_FORMAT_*                               */
   int32_t act_dtype;             /* x, out, fused_out: F32 or BF16            */
   int32_t w_dtype;               /* F32, BF16 or FP8_E4M3                      */
   int32_t act_quant;             /* MOE_QUANT_*; FP8 requires w_dtype FP8      */
   int32_t scoring;               /* MOE_SCORING_*                              */
   int32_t renormalize;           /* divide the k weights by their sum          */
-  int32_t activation;            /* MOE_ACTIVATION_SILU only                  */
-  int32_t apply_router_weight_on_input; /* must be 0                          */
+  int32_t activation;            /* MOE_ACTIVATION_* (routed and shared experts) */
+  int32_t apply_router_weight_on_input; /* 0 or 1 (1 needs topk == 1)        */
   int32_t weight_layout;         /* MOE_WEIGHTS_* of the expert weights        */
   int32_t reserved;              /* must be 0                                  */
-  const int32_t *expert_map;     /* must be NULL (global == local experts)    */
+  const int32_t *expert_map;     /* device int32[global_E] or NULL (identity)  */
 } moe_problem;
 
 /* Expert weights.  w1 [E, N, K], w2 [E, K, N/2] in w_dtype; for FP8_E4M3
@@ -169,8 +187,9 @@ int moe_version(void);
 /* Host-side check of a problem description (the asserts of
  * _moe_problem_size, FusedMoEPermuteExpertsUnpermute.activation and
  * FusedMoEModularKernel.__init__ on the modular_kernel.py page, plus this
- * library's own limits: E <= 1024, topk <= min(E, 64), K % 128 == 0,
- * (N/2) % 64 == 0, fp8 needs (N/2) % 128 == 0, M*topk and E*capacity < 2^31). */
+ * library's own limits: E <= global_E <= 1024, topk <= min(global_E, 64),
+ * K % 128 == 0, (N/2) % 64 == 0, fp8 needs (N/2) % 128 == 0, M*topk and
+ * E*capacity < 2^31; expert_map NULL needs global_E 0 or E). */
 moe_status moe_validate(const moe_problem *p);
 
 /* Workspace needed by any call on this problem (workspace_shapes on the
@@ -186,36 +205,40 @@ moe_status moe_workspace_layout(const moe_problem *p, moe_ws_layout *out);
 moe_status moe_pack_weights(const moe_problem *p, const moe_weights *src, void *w1_packed,
                             void *w2_packed, hipStream_t stream);
 
-/* [Router]: logits [M, E] fp32 -> topk_weights [M, topk] fp32 and topk_ids
- * [M, topk] int32 (the topk_weights / topk_ids that
+/* [Router]: logits [M, global_E] fp32 -> topk_weights [M, topk] fp32 and
+ * topk_ids [M, topk] int32 global ids (the topk_weights / topk_ids that
  * FusedMoEModularKernel.forward consumes).  The topk experts with the largest
  * logits, in descending order, ties to the lower index; weights are the
- * softmax over all E logits or the sigmoid of each, optionally divided by
- * their sum.  NaN logits give unspecified (but in-range) ids. */
+ * softmax over all global_E logits or the sigmoid of each, optionally divided
+ * by their sum.  NaN logits give unspecified (but in-range) ids. */
 moe_status moe_route(const moe_problem *p, const float *logits, float *topk_weights,
                      int32_t *topk_ids, hipStream_t stream);
 
 /* [Quantize-Dispatch] (FusedMoEPrepareAndFinalize.prepare): counts the pairs
- * routed to each expert into expert_num_tokens [E] (ExpertTokensMetadata;
+ * routed to each local expert into expert_num_tokens [E] (ExpertTokensMetadata;
  * device only, no host copy) and lays the pairs out:
  *  STANDARD: a stable counting sort of the M*topk pairs by expert into the
  *    workspace permutation; a_out / a_scale_out receive x quantised per token
- *    group of 128 when act_quant is FP8 ([M, K] codes, [M, K/128] scales) and
- *    must be NULL otherwise (the experts then read x directly).
+ *    group of 128 when act_quant is FP8 ([M, K] codes, [M, K/128] scales), or
+ *    with the router weight on the input w*x in act_dtype ([M, K]), and must
+ *    be NULL otherwise (the experts then read x directly).
  *  BATCHED_EXPERTS: row m of x goes to a_out[e, r, :] for each of its experts
  *    e, r its rank among e's pairs (ascending token); a_out is
  *    [E, max_tokens_per_expert, K] in act_dtype, or fp8 codes with a_scale_out
  *    [E, max_tokens_per_expert, K/128] when act_quant is FP8.  Rows past the
  *    counts are left untouched.  Pairs whose rank reaches the capacity are
  *    dropped and flag MOE_DEVICE_CAPACITY_OVERFLOW.
- * topk_ids with an id outside [0, E) flag MOE_DEVICE_BAD_EXPERT_ID and that
- * pair is ignored. */
-moe_status moe_prepare(const moe_problem *p, const void *x, const int32_t *topk_ids, void *a_out,
-                       float *a_scale_out, int32_t *expert_num_tokens, void *workspace,
-                       size_t workspace_bytes, hipStream_t stream);
+ * topk_weights [M, topk] is read only with apply_router_weight_on_input (else
+ * it may be NULL).  topk_ids with an id outside [0, global_E), or mapped to an
+ * entry outside [-1, E), flag MOE_DEVICE_BAD_EXPERT_ID and that pair is
+ * ignored; picks mapped to -1 belong to other shards and are skipped. */
+moe_status moe_prepare(const moe_problem *p, const void *x, const int32_t *topk_ids,
+                       const float *topk_weights, void *a_out, float *a_scale_out,
+                       int32_t *expert_num_tokens, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream);
 
 /* [Permute-Experts-Unpermute] (FusedMoEPermuteExpertsUnpermute.apply): for
- * each expert, its rows times w1 (gate|up), SiLU(gate) * up, [fp8:
+ * each expert, its rows times w1 (gate|up), act(gate) * up, [fp8:
  * re-quantised per token group], times w2.  `a` is what moe_prepare produced
  * (STANDARD without quantisation: x itself).  expert_num_tokens [E] is read on
  * the device (the masked grouped GEMM of the worst-tokens page).  fused_out
@@ -230,8 +253,10 @@ moe_status moe_experts(const moe_problem *p, const void *a, const float *a_scale
 /* [Combine] (FusedMoEPrepareAndFinalize.finalize with a TopKWeightAndReduce):
  * out[m, :] = sum_j topk_weights[m, j] * fused_out[pair (m, j), :], summed in
  * fp32 in j order, written in act_dtype; out [M, K] is fully overwritten.
- * BATCHED_EXPERTS reads the pair -> row map moe_prepare left in the
- * workspace; dropped pairs contribute nothing. */
+ * BATCHED_EXPERTS, and STANDARD with an expert_map, read the pair -> row map
+ * moe_prepare left in the workspace; dropped pairs and other shards' picks
+ * contribute nothing.  With apply_router_weight_on_input the weights are not
+ * applied again (topk_weights may be NULL). */
 moe_status moe_finalize(const moe_problem *p, const void *fused_out, const float *topk_weights,
                         void *out, void *workspace, size_t workspace_bytes, hipStream_t stream);
 

@@ -27,7 +27,8 @@ def torch_act_dtype(wl):
 def problem(wl, **over) -> moe.Problem:
     kw = dict(format=wl.format, act_dtype=wl.act_dtype, w_dtype=wl.w_dtype, act_quant=wl.act_quant,
               scoring=wl.scoring, renormalize=wl.renormalize, max_tokens_per_expert=wl.capacity,
-              shared_N=2 * wl.shared_I)
+              shared_N=2 * wl.shared_I, activation=wl.activation,
+              apply_router_weight_on_input=wl.router_weight_on_input, global_E=wl.global_E)
     kw.update(over)
     return moe.make_problem(wl.E, wl.M, 2 * wl.I, wl.K, wl.topk, **kw)
 
@@ -45,8 +46,9 @@ def rel_err(got, ref) -> float:
 
 
 def run_forward(wl, d, ws=None, p=None, out=None, shared_out=None, streams=None):
-    """Whole layer through moe_forward; returns (out, shared_out or None, ws, problem)."""
-    p = p or problem(wl)
+    """Whole layer through moe_forward; returns (out, shared_out or None, ws, problem).
+    d may hold "expert_map" (device int32 [global_E]) for an expert-parallel shard."""
+    p = p or problem(wl, expert_map=d.get("expert_map"))
     if ws is None:
         ws = moe.empty_workspace(p)
     if out is None:

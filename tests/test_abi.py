@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = moe.load_library()
-    assert L.moe_version() == 1
+    assert L.moe_version() == 2
     assert moe.status_str(moe.MOE_OK) == "ok"
     assert "workspace" in moe.status_str(moe.MOE_ERR_WORKSPACE)
 
@@ -46,7 +46,8 @@ _LAYOUT_PROBE = r"""
 #define F(T, f) printf(#T "." #f " %zu\n", offsetof(T, f));
 int main(void) {
   printf("moe_problem %zu\n", sizeof(moe_problem));
-  F(moe_problem, E) F(moe_problem, max_tokens_per_expert) F(moe_problem, shared_N) F(moe_problem, format)
+  F(moe_problem, E) F(moe_problem, max_tokens_per_expert) F(moe_problem, shared_N) F(moe_problem, global_E)
+  F(moe_problem, format)
   F(moe_problem, apply_router_weight_on_input) F(moe_problem, weight_layout) F(moe_problem, expert_map)
   printf("moe_weights %zu\n", sizeof(moe_weights));
   printf("moe_shared %zu\n", sizeof(moe_shared));
@@ -128,11 +129,31 @@ def test_validation_status_codes():
     p = moe.make_problem(**base, act_dtype=moe.DTYPE_F32)                     # mixed f32 x bf16
     assert moe.validate(p) == moe.MOE_ERR_UNSUPPORTED
     p = moe.make_problem(**base)
-    p.activation = 1                                                          # only silu
+    p.activation = 2                                                          # silu or gelu only
     assert moe.validate(p) == moe.MOE_ERR_UNSUPPORTED
+    assert moe.validate(moe.make_problem(**base, activation=moe.ACTIVATION_GELU)) == moe.MOE_OK
+    p = moe.make_problem(**base, apply_router_weight_on_input=True)          # needs topk == 1
+    assert moe.validate(p) == moe.MOE_ERR_INVALID_ARG
+    p = moe.make_problem(**dict(base, topk=1), apply_router_weight_on_input=True)
+    assert moe.validate(p) == moe.MOE_OK
     p = moe.make_problem(**base)
-    p.apply_router_weight_on_input = 1
+    p.apply_router_weight_on_input = 2
+    assert moe.validate(p) == moe.MOE_ERR_INVALID_ARG
+    # expert-parallel shard: global_E without a map, local experts above global
+    assert moe.validate(moe.make_problem(**base, global_E=16)) == moe.MOE_ERR_INVALID_ARG
+    p = moe.make_problem(**base, global_E=16)
+    p.expert_map = 0x1000                                                     # any device pointer
+    assert moe.validate(p) == moe.MOE_OK
+    p = moe.make_problem(**dict(base, E=20), global_E=16)
+    p.expert_map = 0x1000
+    assert moe.validate(p) == moe.MOE_ERR_INVALID_ARG
+    p = moe.make_problem(**dict(base, E=4, topk=6), global_E=16)             # topk bounded by global_E
+    p.expert_map = 0x1000
+    assert moe.validate(p) == moe.MOE_OK
+    p = moe.make_problem(**base, global_E=2048)
+    p.expert_map = 0x1000
     assert moe.validate(p) == moe.MOE_ERR_UNSUPPORTED
+    assert moe.validate(moe.make_problem(**base, global_E=-1)) == moe.MOE_ERR_INVALID_ARG
     p = moe.make_problem(**base)
     p.scoring = 7
     assert moe.validate(p) == moe.MOE_ERR_INVALID_ARG
@@ -149,9 +170,15 @@ def test_host_errors_need_no_gpu():
     p = moe.make_problem(E=8, M=16, N=256, K=256, topk=2)
     ws_size = moe.workspace_size(p)
     assert L.moe_route(C.byref(p), None, None, None, None) == moe.MOE_ERR_INVALID_ARG
-    assert L.moe_prepare(C.byref(p), None, None, None, None, None, None, 0, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_prepare(C.byref(p), None, None, None, None, None, None, None, 0, None) == moe.MOE_ERR_INVALID_ARG
     fake = C.c_void_p(0x1000)
-    assert L.moe_prepare(C.byref(p), fake, fake, None, None, fake, fake, ws_size - 1, None) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_prepare(C.byref(p), fake, fake, None, None, None, fake, fake, ws_size - 1, None) \
+        == moe.MOE_ERR_WORKSPACE
+    # router weight on the input: prepare needs the weights and an a_out
+    p1 = moe.make_problem(E=8, M=16, N=256, K=256, topk=1, apply_router_weight_on_input=True)
+    ws1 = moe.workspace_size(p1)
+    assert L.moe_prepare(C.byref(p1), fake, fake, None, fake, None, fake, fake, ws1, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_prepare(C.byref(p1), fake, fake, fake, None, None, fake, fake, ws1, None) == moe.MOE_ERR_INVALID_ARG
     w = moe.Weights(None, None, None, None)
     assert L.moe_experts(C.byref(p), fake, None, C.byref(w), fake, fake, fake, ws_size, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_finalize(C.byref(p), None, None, None, fake, ws_size, None) == moe.MOE_ERR_INVALID_ARG

@@ -554,3 +554,124 @@ def test_packed_weights_full_size(name):
     err = U.rel_err(got.float().cpu().numpy()[toks], oref)
     print(f"  {name} packed: max rel err {err:.3e}", flush=True)
     assert err <= U.tol_for(wl)
+
+
+# ----------------------------------------- GELU, expert-parallel shard, router weight on input
+
+GELU_CASES = {
+    "f32_tiled": WORKLOADS["tiny_fp32"].replace(activation=1),
+    "bf16_stream": WORKLOADS["mixtral_bf16"].replace(M=300, K=384, I=256, E=7, topk=3, renormalize=False,
+                                                     logits_dist="normal", activation=1),
+    "bf16_mfma_shared": WORKLOADS["dsv3_bf16"].replace(M=520, K=512, I=256, E=4, topk=2, shared_I=256,
+                                                       activation=1),
+    "fp8_batched": WORKLOADS["decode_fp8_m64"].replace(M=90, K=384, I=256, E=5, topk=2, capacity=90,
+                                                       activation=1),
+}
+
+
+@pytest.mark.parametrize("name", list(GELU_CASES))
+def test_gelu_forward_parity(name):
+    """gelu_and_mul in every gated epilogue (tiled, streaming with fp8
+    re-quantisation, 256x256 MFMA, shared expert)."""
+    wl = GELU_CASES[name]
+    d = make_inputs(wl, seed=31, device="cpu")
+    out, sout, _, _ = U.run_forward(wl, U.to_cuda(d))
+    torch.cuda.synchronize()
+    toks = sample_tokens(wl.M, 24, seed=5)
+    ref, _, _ = oracle.moe_tokens(wl, d, toks)
+    err = U.rel_err(out.float().cpu().numpy()[toks], ref)
+    print(f"  gelu {name}: max rel err {err:.3e}", flush=True)
+    assert err <= U.tol_for(wl)
+    if wl.shared_I:
+        sref = oracle.dense_mlp_tokens(d["x"], d["w1s"], d["w2s"], wl.shared_I, wl.act_dtype, toks,
+                                       activation=1)
+        serr = U.rel_err(sout.float().cpu().numpy()[toks], sref)
+        print(f"  gelu {name} shared: max rel err {serr:.3e}", flush=True)
+        assert serr <= U.tol_for(wl)
+
+
+SHARD_CASES = {
+    "bf16_standard": WORKLOADS["mixtral_bf16"].replace(M=200, K=384, I=256, E=12, topk=3, renormalize=True,
+                                                       logits_dist="normal"),
+    "bf16_batched": WORKLOADS["mixtral_bf16"].replace(M=150, K=256, I=128, E=12, topk=2, format=FORMAT_BATCHED,
+                                                      capacity=150, logits_dist="normal"),
+    "fp8_batched": WORKLOADS["decode_fp8_m64"].replace(M=80, K=256, I=256, E=12, topk=4, capacity=80),
+}
+
+
+def _shard_inputs(d, Eg, n_shards, s):
+    """Shard s of n: global experts g with g % n == s, local index g // n."""
+    glob = torch.arange(Eg)[torch.arange(Eg) % n_shards == s]
+    emap = torch.full((Eg,), -1, dtype=torch.int32)
+    emap[glob] = torch.arange(glob.numel(), dtype=torch.int32)
+    out = dict(d, w1=d["w1"][glob].contiguous(), w2=d["w2"][glob].contiguous(), expert_map=emap)
+    for k in ("w1_scale", "w2_scale"):
+        if d.get(k) is not None:
+            out[k] = d[k][glob].contiguous()
+    return out, glob.numel()
+
+
+@pytest.mark.parametrize("name", list(SHARD_CASES))
+def test_expert_parallel_shards(name):
+    """Three expert-parallel shards (expert_map): each matches the oracle's
+    shard; the routing ids are global; the shards' outputs sum to the
+    unsharded layer's."""
+    wl = SHARD_CASES[name]
+    Eg = wl.E
+    d = make_inputs(wl, seed=32, device="cpu")
+    full, _, fws, _ = U.run_forward(wl, U.to_cuda(d))
+    torch.cuda.synchronize()
+    total = torch.zeros_like(full, dtype=torch.float32)
+    toks = sample_tokens(wl.M, 20, seed=6)
+    for s in range(3):
+        ds, El = _shard_inputs(d, Eg, 3, s)
+        wls = wl.replace(E=El, global_E=Eg)
+        out, _, ws, p = U.run_forward(wls, U.to_cuda(ds))
+        torch.cuda.synchronize()
+        L = moe.workspace_layout(p)
+        ids = U.ws_view(ws, L.topk_ids, wl.M * wl.topk).cpu().numpy()
+        fids = U.ws_view(fws, moe.workspace_layout(U.problem(wl)).topk_ids, wl.M * wl.topk).cpu().numpy()
+        np.testing.assert_array_equal(ids, fids)
+        counts = U.ws_view(ws, L.counts, El).cpu().numpy()
+        local = ds["expert_map"].numpy()[ids]
+        np.testing.assert_array_equal(counts, np.bincount(local[local >= 0], minlength=El))
+        assert (U.ws_view(ws, L.status, 1).item() & moe.DEVICE_BAD_EXPERT_ID) == 0
+        ref, _, _ = oracle.moe_tokens(wls, ds, toks)
+        err = U.rel_err(out.float().cpu().numpy()[toks], ref)
+        print(f"  shard {name} {s}: max rel err {err:.3e}", flush=True)
+        assert err <= U.tol_for(wl)
+        total += out.float()
+    err = U.rel_err(total.cpu().numpy(), full.float().cpu().numpy())
+    print(f"  shards {name} sum vs unsharded: max rel err {err:.3e}", flush=True)
+    assert err <= U.tol_for(wl)
+
+
+WOI_CASES = {
+    "f32": WORKLOADS["tiny_fp32"].replace(topk=1, renormalize=False, router_weight_on_input=True),
+    "bf16_stream": WORKLOADS["mixtral_bf16"].replace(M=300, K=384, I=256, E=6, topk=1, renormalize=False,
+                                                     logits_dist="normal", router_weight_on_input=True),
+    "bf16_batched": WORKLOADS["mixtral_bf16"].replace(M=150, K=256, I=128, E=5, topk=1, format=FORMAT_BATCHED,
+                                                      capacity=150, logits_dist="normal", renormalize=False,
+                                                      router_weight_on_input=True),
+    "fp8_batched": WORKLOADS["decode_fp8_m64"].replace(M=90, K=384, I=256, E=5, topk=1, capacity=90,
+                                                       renormalize=False, router_weight_on_input=True),
+}
+
+
+@pytest.mark.parametrize("name", list(WOI_CASES))
+def test_router_weight_on_input_parity(name):
+    """topk = 1 with the router weight applied to the input before
+    quantisation / dispatch, and not again in the combine."""
+    wl = WOI_CASES[name]
+    d = make_inputs(wl, seed=33, device="cpu")
+    out, _, _, _ = U.run_forward(wl, U.to_cuda(d))
+    torch.cuda.synchronize()
+    toks = sample_tokens(wl.M, 24, seed=7)
+    ref, _, w = oracle.moe_tokens(wl, d, toks)
+    assert np.all(w < 1.0)
+    err = U.rel_err(out.float().cpu().numpy()[toks], ref)
+    print(f"  weight on input {name}: max rel err {err:.3e}", flush=True)
+    assert err <= U.tol_for(wl)
+    # the weight is applied once: against the plain layer the output differs
+    plain, _, _ = oracle.moe_tokens(wl.replace(router_weight_on_input=False), d, toks)
+    assert U.rel_err(plain, ref) > 10 * U.tol_for(wl)
