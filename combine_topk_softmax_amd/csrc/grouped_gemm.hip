@@ -1,9 +1,9 @@
 // [Permute-Experts-Unpermute]: the two grouped expert GEMMs on gfx950 MFMA.
 //
-// The modular_kernel.py page describes the experts step as "matmul + act_mul
-// + optionally quant + matmul" (header comment) with
-// FusedMoEPermuteExpertsUnpermute.activation applying silu_and_mul, whose
-// output is half as wide as its input; the worst-tokens page has the grouped
+// The modular_kernel.py page's header comment splits the experts step into a
+// first GEMM, the gated activation (FusedMoEPermuteExpertsUnpermute
+// .activation, silu_and_mul, whose output is half as wide as its input), an
+// optional quantisation and a second GEMM; the worst-tokens page has the grouped
 // GEMM read the per-expert counts from a device tensor.  Here:
 //
 //   gated GEMM   act[slot, j] = silu(A w1[e, j]) * (A w1[e, I + j])

@@ -1,8 +1,8 @@
 // Compute-bound grouped expert GEMMs (bf16) for prefill batches whose experts
 // hold many rows: the same two products as grouped_gemm.hip (modular_kernel.py
-// page, FusedMoEPermuteExpertsUnpermute: "matmul + act_mul + optionally quant
-// + matmul"; per-expert row counts read on the device, as on the worst-tokens
-// page),
+// page, header comment and FusedMoEPermuteExpertsUnpermute: a first GEMM, the
+// gated activation, optional quantisation, a second GEMM; per-expert row
+// counts read on the device, as on the worst-tokens page),
 //
 //   gated GEMM   act[slot, j] = silu(A w1[e, j]) * (A w1[e, I + j])
 //   down GEMM    out[row(slot), :] = act[slot, :] w2[e]^T

@@ -2,11 +2,11 @@
 // per expert at most): decode-sized batches and prefill whose per-expert row
 // count is below the MFMA/HBM ridge.  Same computation as grouped_gemm.hip --
 // the gated GEMM act = silu(A w1_gate) * (A w1_up) or the down GEMM
-// out = act w2^T with the unpermute in its epilogue (modular_kernel.py page:
-// FusedMoEPermuteExpertsUnpermute, "matmul + act_mul + optionally quant +
-// matmul"; the worst-tokens page: the grouped GEMM is masked by per-expert
-// counts read on the device) -- organised around reading every weight byte
-// exactly once:
+// out = act w2^T with the unpermute in its epilogue (modular_kernel.py page,
+// FusedMoEPermuteExpertsUnpermute: GEMM, gated activation, optional
+// quantisation, GEMM; the worst-tokens page: the grouped GEMM is masked by
+// per-expert counts read on the device) -- organised around reading every
+// weight byte exactly once:
 //
 //  * one workgroup = one expert's rows (up to TMAX, masked by the device
 //    count in 16-row MFMA blocks) x a panel of weight rows, so an expert's

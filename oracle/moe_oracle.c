@@ -112,8 +112,8 @@ void oracle_e4m3_decode_array(int64_t n, const uint8_t *c, double *out) {
 }
 
 /* Per-token-group quantisation with group 128 ([MK] FusedMoEPrepareAndFinalize
- * .prepare "perform any quantization", quant_config block_shape /
- * per_act_token_quant; the a2 scale keeps the second GEMM's input quantised
+ * .prepare, which quantises the input as the quant config asks (block_shape /
+ * per_act_token_quant); the a2 scale keeps the second GEMM's input quantised
  * the same way).  x is [rows, cols] fp32, q [rows, cols], s [rows, cols/128]. */
 void oracle_quant_g128(int64_t rows, int64_t cols, const float *x, uint8_t *q, float *s) {
   int64_t G = cols / 128;
@@ -256,9 +256,10 @@ void oracle_permute_batched(int64_t n, const int32_t *ids, int64_t E, int64_t ca
 
 /* ------------------------------------------------------------ expert MLP */
 
-/* One expert on one input row ([MK] header: "matmul + act_mul + optionally
- * quant + matmul"; FusedMoEPermuteExpertsUnpermute.activation: silu_and_mul,
- * whose output is half the width of its input).
+/* One expert on one input row ([MK] header comment: a GEMM, the gated
+ * activation, optional quantisation, a second GEMM;
+ * FusedMoEPermuteExpertsUnpermute.activation: silu_and_mul, whose output is
+ * half the width of its input).
  *   h   = W1[e] a            (2I values; gate = h[0:I], up = h[I:2I])
  *   act = silu(gate) * up,   silu(z) = z / (1 + exp(-z))
  *      or gelu(gate) * up,   gelu(z) = 0.5 z (1 + erf(z / sqrt 2))  (gelu_and_mul)
@@ -315,8 +316,9 @@ static float round_bf16(float v) {
 }
 
 /* Element c of token m's input row: x itself, or with the router weight on
- * the input ([MK] prepare: "apply the weights to the activations, before
- * quantization + dispatching") w * x held in the activation dtype. */
+ * the input ([MK] prepare: with the flag set, the weights scale the
+ * activations ahead of quantisation and dispatch) w * x held in the
+ * activation dtype. */
 static double input_value(int act_dtype, const void *x, int64_t K, int64_t m, int64_t c, int weighted,
                           float w) {
   double v = act_at(act_dtype, x, m * K + c);
