@@ -303,32 +303,40 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
         }
       } else {
         // fp8: one MFMA step per K-step and block.  Blocks in order, A fragments
-        // read kAhead blocks ahead (pinned like the bf16 ring), each block's
-        // partial sums scaled by its row and weight-block scales right after
-        // its MFMAs.
+        // read kAhead blocks ahead (pinned like the bf16 ring); a block's
+        // partial sums are scaled by its row and weight-block scales and folded
+        // after the next block's MFMAs are issued, so the FMAs never wait on
+        // the MFMA that produced them.
         static_assert(MM::kSteps == 1, "scaled path: one MFMA step per K-step");
         constexpr int kAhead = MOE_STREAM_FRAG_AHEAD < NMB ? MOE_STREAM_FRAG_AHEAD : NMB;
         frag f[NMB];
+        f32x4 part[2][NBW];
 #pragma unroll
         for (int x = 0; x < kAhead; ++x) f[x] = lds_frag<frag>(A, x * 16 + r16, q * 32);
-#pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) {
-          if (mb + kAhead < NMB) f[mb + kAhead] = lds_frag<frag>(A, (mb + kAhead) * 16 + r16, q * 32);
-          f32x4 part[NBW];
+        auto issue = [&](int mb) {
 #pragma unroll
           for (int b = 0; b < NBW; ++b)
-            part[b] = MM::mma(f[mb], frag_at<frag>(wb[j][b], 0), f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+            part[mb & 1][b] = MM::mma(f[mb], frag_at<frag>(wb[j][b], 0), f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+        };
+        auto fold = [&](int mb) {
           const float4 sa4 = *reinterpret_cast<const float4 *>(&Sa[st][mb * 16 + q * 4]);
           const float sa[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int b = 0; b < NBW; ++b) acc[mb][b][i] += part[b][i] * (sa[i] * wsv[j][b]);
-          // Fold each block's partial sums here: without this the compiler
-          // sinks all blocks' scale FMAs to the end of the K-step and keeps
-          // every block's partial sums live at once.
+            for (int b = 0; b < NBW; ++b) acc[mb][b][i] += part[mb & 1][b][i] * (sa[i] * wsv[j][b]);
+          // Fold each block here: without this the compiler sinks all blocks'
+          // scale FMAs to the end of the K-step and keeps every block's partial
+          // sums live at once.
 #pragma unroll
           for (int b = 0; b < NBW; ++b) asm volatile("" : "+v"(acc[mb][b]));
+        };
+        issue(0);
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+          if (mb + kAhead < NMB) f[mb + kAhead] = lds_frag<frag>(A, (mb + kAhead) * 16 + r16, q * 32);
+          if (mb + 1 < NMB) issue(mb + 1);
+          fold(mb);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
