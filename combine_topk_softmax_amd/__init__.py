@@ -40,7 +40,7 @@ class Problem(C.Structure):
     _fields_ = [
         ("E", C.c_int64), ("M", C.c_int64), ("N", C.c_int64), ("K", C.c_int64),
         ("topk", C.c_int64), ("max_tokens_per_expert", C.c_int64), ("align", C.c_int64),
-        ("shared_N", C.c_int64), ("global_E", C.c_int64),
+        ("shared_N", C.c_int64), ("global_E", C.c_int64), ("chunk_tokens", C.c_int64),
         ("format", C.c_int32), ("act_dtype", C.c_int32), ("w_dtype", C.c_int32),
         ("act_quant", C.c_int32), ("scoring", C.c_int32), ("renormalize", C.c_int32),
         ("activation", C.c_int32), ("apply_router_weight_on_input", C.c_int32),
@@ -137,13 +137,13 @@ def make_problem(E, M, N, K, topk, *, format=FORMAT_STANDARD, act_dtype=DTYPE_BF
                  act_quant=QUANT_NONE, scoring=SCORING_SOFTMAX, renormalize=False,
                  max_tokens_per_expert=0, align=0, shared_N=0, weight_layout=WEIGHTS_ROW_MAJOR,
                  activation=ACTIVATION_SILU, apply_router_weight_on_input=False, global_E=0,
-                 expert_map: Optional[torch.Tensor] = None) -> Problem:
+                 expert_map: Optional[torch.Tensor] = None, chunk_tokens=0) -> Problem:
     """expert_map: device int32 tensor [global_E] (local expert or -1); the
     caller keeps it alive while the problem is in use."""
     if expert_map is not None and (expert_map.dtype != torch.int32 or expert_map.numel() != (global_E or E)):
         raise ValueError("expert_map must be an int32 tensor of global_E entries")
     return Problem(E=E, M=M, N=N, K=K, topk=topk, max_tokens_per_expert=max_tokens_per_expert, align=align,
-                   shared_N=shared_N, global_E=global_E, format=format, act_dtype=act_dtype, w_dtype=w_dtype,
+                   shared_N=shared_N, global_E=global_E, chunk_tokens=chunk_tokens, format=format, act_dtype=act_dtype, w_dtype=w_dtype,
                    act_quant=act_quant, scoring=scoring, renormalize=int(renormalize), activation=activation,
                    apply_router_weight_on_input=int(apply_router_weight_on_input), weight_layout=weight_layout,
                    reserved=0, expert_map=_ptr(expert_map))

@@ -78,10 +78,10 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t *__restrict__ chunk_
                                                     int32_t *counts, int32_t *expert_num_tokens,
                                                     int32_t *__restrict__ offsets,
                                                     int32_t *__restrict__ perm, int64_t perm_len,
-                                                    int32_t *__restrict__ status) {
+                                                    int32_t *__restrict__ status, int clear_status) {
   __shared__ int total_sh;
   const int e = threadIdx.x;
-  if (e == 0) *status = 0;
+  if (e == 0 && clear_status) *status = 0;
   int run = 0;
   if (e < E) {
     for (int c = 0; c < n_chunks; ++c) {
@@ -341,7 +341,7 @@ hipError_t launch_count_and_permute(const moe_problem &p, const int32_t *ids,
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   scan_kernel<<<1, 1024, 0, s>>>(b.chunk_hist, (int)b.n_chunks, E, align, standard, b.counts,
-                                 expert_num_tokens, b.offsets, b.perm, b.perm_len, b.status);
+                                 expert_num_tokens, b.offsets, b.perm, b.perm_len, b.status, b.clear_status);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   rank_kernel<<<(unsigned)b.n_chunks, 64, 0, s>>>(ids, n, E, Eg, p.expert_map, ceil_log2(E), (int)b.chunk, standard,

@@ -32,7 +32,8 @@ moe_status validate(const moe_problem *pp) {
   if (!pp) return MOE_ERR_INVALID_ARG;
   const moe_problem &p = *pp;
   if (p.E < 1 || p.M < 0 || p.N < 2 || p.K < 1 || p.topk < 1) return MOE_ERR_INVALID_ARG;
-  if (p.global_E < 0) return MOE_ERR_INVALID_ARG;
+  if (p.global_E < 0 || p.chunk_tokens < 0) return MOE_ERR_INVALID_ARG;
+  if (p.chunk_tokens > 0 && p.format != MOE_FORMAT_STANDARD) return MOE_ERR_UNSUPPORTED;
   const int64_t Eg = router_width(p);
   if (p.N % 2 != 0 || p.topk > Eg || p.E > Eg) return MOE_ERR_INVALID_ARG;
   if (!p.expert_map && Eg != p.E) return MOE_ERR_INVALID_ARG;   // no map: global == local
@@ -69,9 +70,15 @@ moe_status validate(const moe_problem *pp) {
   return MOE_OK;
 }
 
+// Tokens whose intermediates the workspace holds at once: one chunk when the
+// experts step is chunked, else the whole batch.
+int64_t chunk_of(const moe_problem &p) { return p.chunk_tokens > 0 ? std::min(p.M, p.chunk_tokens) : p.M; }
+bool chunked(const moe_problem &p) { return p.chunk_tokens > 0 && p.chunk_tokens < p.M; }
+
 void layout(const moe_problem &p, moe_ws_layout &L) {
   memset(&L, 0, sizeof(L));
-  const int64_t n = p.M * p.topk;
+  const int64_t n = p.M * p.topk;        // pairs of the batch
+  const int64_t nc = chunk_of(p) * p.topk;   // pairs of one chunk
   const int64_t E = p.E, I = p.N / 2;
   const bool standard = p.format == MOE_FORMAT_STANDARD;
   const int64_t align = p.align > 0 ? p.align : 1;
@@ -79,11 +86,11 @@ void layout(const moe_problem &p, moe_ws_layout &L) {
   const int64_t eb = act_elem_bytes(p.act_dtype);
   const bool fp8 = fp8_path(p);
 
-  L.perm_len = standard ? n + E * (align - 1) : 0;
-  L.chunk = std::max<int64_t>(1024, round_up((n + 63) / 64, 256));
-  L.n_chunks = std::max<int64_t>(1, (n + L.chunk - 1) / L.chunk);
+  L.perm_len = standard ? nc + E * (align - 1) : 0;
+  L.chunk = std::max<int64_t>(1024, round_up((nc + 63) / 64, 256));
+  L.n_chunks = std::max<int64_t>(1, (nc + L.chunk - 1) / L.chunk);
   L.tile_rows = kTileRows;
-  const int64_t tiled_rows = standard ? n : std::min(n, E * cap);
+  const int64_t tiled_rows = standard ? nc : std::min(n, E * cap);
   L.max_tiles = std::max<int64_t>(1, (tiled_rows + E * (kTileRows - 1)) / kTileRows);
   L.act_rows = standard ? L.perm_len : E * cap;
 
@@ -142,25 +149,42 @@ bool prepared_rows(const moe_problem &p) {
          p.apply_router_weight_on_input;
 }
 
-moe_status do_prepare(const moe_problem &p, const void *x, const int32_t *ids, const float *topk_w,
-                      void *a_out, float *a_scale_out, int32_t *expert_num_tokens, void *ws,
-                      const moe_ws_layout &L, hipStream_t s) {
+// Counts and permutation of p.M tokens' pairs (ids), their pair -> slot map
+// written from inv_pair0 on (a chunk's pairs within the batch's map).
+moe_status do_count(const moe_problem &p, const int32_t *ids, int32_t *expert_num_tokens, void *ws,
+                    const moe_ws_layout &L, int64_t inv_pair0, hipStream_t s) {
   DispatchBufs b;
   b.status = at<int32_t>(ws, L.status);
   b.counts = at<int32_t>(ws, L.counts);
   b.offsets = at<int32_t>(ws, L.offsets);
   b.chunk_hist = at<int32_t>(ws, L.chunk_hist);
   b.perm = at<int32_t>(ws, L.perm);
-  b.inv = at<int32_t>(ws, L.inv);
+  b.inv = at<int32_t>(ws, L.inv) + inv_pair0;
   b.perm_len = L.perm_len;
   b.n_chunks = L.n_chunks;
   b.chunk = L.chunk;
+  b.clear_status = inv_pair0 == 0;
   MOE_HIP(launch_count_and_permute(p, ids, expert_num_tokens, b, s));
-  const bool batched = p.format == MOE_FORMAT_BATCHED_EXPERTS;
-  if (prepared_rows(p))
-    MOE_HIP(launch_dispatch_rows(p, x, b.inv, p.apply_router_weight_on_input ? topk_w : nullptr, a_out,
-                                 a_scale_out, batched, s));
   return MOE_OK;
+}
+
+// The rows the experts read, when prepare writes them (quantised, batched or
+// router-weighted); the batched scatter reads the pair -> row map.
+moe_status do_rows(const moe_problem &p, const void *x, const float *topk_w, void *a_out, float *a_scale_out,
+                   void *ws, const moe_ws_layout &L, hipStream_t s) {
+  if (!prepared_rows(p)) return MOE_OK;
+  const bool batched = p.format == MOE_FORMAT_BATCHED_EXPERTS;
+  MOE_HIP(launch_dispatch_rows(p, x, at<int32_t>(ws, L.inv), p.apply_router_weight_on_input ? topk_w : nullptr,
+                               a_out, a_scale_out, batched, s));
+  return MOE_OK;
+}
+
+moe_status do_prepare(const moe_problem &p, const void *x, const int32_t *ids, const float *topk_w,
+                      void *a_out, float *a_scale_out, int32_t *expert_num_tokens, void *ws,
+                      const moe_ws_layout &L, hipStream_t s) {
+  moe_status st = do_count(p, ids, expert_num_tokens, ws, L, 0, s);
+  if (st != MOE_OK) return st;
+  return do_rows(p, x, topk_w, a_out, a_scale_out, ws, L, s);
 }
 
 moe_status do_experts(const moe_problem &p, const void *a, const float *a_scale, const moe_weights &w,
@@ -363,6 +387,7 @@ moe_status moe_prepare(const moe_problem *p, const void *x, const int32_t *topk_
   moe_status st = validate(p);
   if (st != MOE_OK) return st;
   if (p->M == 0) return MOE_OK;
+  if (chunked(*p)) return MOE_ERR_UNSUPPORTED;   // chunking is moe_forward's
   moe_ws_layout L;
   if ((st = check_ws(*p, workspace, workspace_bytes, L)) != MOE_OK) return st;
   if (!x || !topk_ids || !expert_num_tokens) return MOE_ERR_INVALID_ARG;
@@ -382,6 +407,7 @@ moe_status moe_experts(const moe_problem *p, const void *a, const float *a_scale
   moe_status st = validate(p);
   if (st != MOE_OK) return st;
   if (p->M == 0) return MOE_OK;
+  if (chunked(*p)) return MOE_ERR_UNSUPPORTED;
   moe_ws_layout L;
   if ((st = check_ws(*p, workspace, workspace_bytes, L)) != MOE_OK) return st;
   if (!a || !w || !w->w1 || !w->w2 || !expert_num_tokens || !fused_out) return MOE_ERR_INVALID_ARG;
@@ -454,11 +480,29 @@ moe_status moe_forward(const moe_problem *p, const float *logits, const void *x,
   void *a_q = prepared_rows(*p) ? at<void>(workspace, L.a_q) : nullptr;
   float *a_s = quant ? at<float>(workspace, L.a_scale) : nullptr;
   int32_t *counts = at<int32_t>(workspace, L.counts);
-  if ((st = do_prepare(*p, x, ti, tw, a_q, a_s, counts, workspace, L, stream)) != MOE_OK) return st;
-
   void *fused = at<void>(workspace, L.fused_out);
-  if ((st = do_experts(*p, a_q ? a_q : x, a_s, *w, counts, fused, workspace, L, stream, events)) != MOE_OK)
-    return st;
+  if (!chunked(*p)) {
+    if ((st = do_prepare(*p, x, ti, tw, a_q, a_s, counts, workspace, L, stream)) != MOE_OK) return st;
+    if ((st = do_experts(*p, a_q ? a_q : x, a_s, *w, counts, fused, workspace, L, stream, events)) != MOE_OK)
+      return st;
+  } else {
+    // Prepare the whole batch's rows, then count, permute and run the experts
+    // chunk by chunk (stage events then mark the last chunk's boundaries).
+    if ((st = do_rows(*p, x, tw, a_q, a_s, workspace, L, stream)) != MOE_OK) return st;
+    const int64_t a_row_bytes = a_q ? (quant ? p->K : p->K * act_elem_bytes(p->act_dtype))
+                                    : p->K * act_elem_bytes(p->act_dtype);
+    const int64_t out_row_bytes = p->K * act_elem_bytes(p->act_dtype);
+    for (int64_t m0 = 0; m0 < p->M; m0 += p->chunk_tokens) {
+      moe_problem pc = *p;
+      pc.M = std::min(p->chunk_tokens, p->M - m0);
+      const int64_t pair0 = m0 * p->topk;
+      if ((st = do_count(pc, ti + pair0, counts, workspace, L, pair0, stream)) != MOE_OK) return st;
+      const uint8_t *a = reinterpret_cast<const uint8_t *>(a_q ? a_q : x) + m0 * a_row_bytes;
+      const float *as = a_s ? a_s + m0 * (p->K / 128) : nullptr;
+      void *fo = reinterpret_cast<uint8_t *>(fused) + pair0 * out_row_bytes;
+      if ((st = do_experts(pc, a, as, *w, counts, fo, workspace, L, stream, events)) != MOE_OK) return st;
+    }
+  }
   // the permutation prepare just wrote masks dropped / other shards' pairs
   MOE_HIP(launch_combine(*p, fused, p->apply_router_weight_on_input ? nullptr : tw,
                          at<int32_t>(workspace, L.inv), !standard, out, stream));

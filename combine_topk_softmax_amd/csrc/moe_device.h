@@ -194,6 +194,7 @@ hipError_t launch_route(const moe_problem &p, const float *logits, float *w, int
 struct DispatchBufs {
   int32_t *status, *counts, *offsets, *chunk_hist, *perm, *inv;
   int64_t perm_len, n_chunks, chunk;
+  int clear_status;   // reset the status word first (not for the later chunks of one batch)
 };
 
 hipError_t launch_count_and_permute(const moe_problem &p, const int32_t *ids, int32_t *expert_num_tokens,

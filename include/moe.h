@@ -93,6 +93,14 @@ enum { MOE_DEVICE_BAD_EXPERT_ID = 1, MOE_DEVICE_CAPACITY_OVERFLOW = 2 };
  * the shards' outputs sum to the unsharded layer's.  expert_map NULL and
  * global_E 0 (or E) is the plain one-shard layer.
  *
+ * Activation chunking (the page's _maybe_chunk_fused_experts): with
+ * 0 < chunk_tokens < M, moe_forward routes and prepares the whole batch, then
+ * runs the experts step chunk by chunk (per-chunk recount, permutation, tile
+ * plan and GEMMs) into slices of the full (M, topk, K) expert output, and
+ * combines once.  The workspace then holds one chunk's intermediates.  The
+ * STANDARD format only; the stage calls moe_prepare / moe_experts need an
+ * unchunked problem.  Each token's result is the same as unchunked.
+ *
  * apply_router_weight_on_input (topk == 1 only; FusedMoEModularKernel.forward
  * on the page): prepare multiplies each token's input row by its router
  * weight, rounded to act_dtype, before any quantisation, and the combine adds
@@ -107,6 +115,7 @@ typedef struct moe_problem {
   int64_t align;                 /* STANDARD: pad expert segments to this (0 = 1) */
   int64_t shared_N;              /* rows of the shared expert's w1 (2*I_s); 0 = none */
   int64_t global_E;              /* router width (experts in the global space); 0 = E */
+  int64_t chunk_tokens;          /* moe_forward: experts step in chunks of this many tokens (0 = all) */
   int32_t format;                /* MOE_FORMAT_*                               */
   int32_t act_dtype;             /* x, out, fused_out: F32 or BF16            */
   int32_t w_dtype;               /* F32, BF16 or FP8_E4M3                      */

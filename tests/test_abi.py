@@ -47,6 +47,7 @@ _LAYOUT_PROBE = r"""
 int main(void) {
   printf("moe_problem %zu\n", sizeof(moe_problem));
   F(moe_problem, E) F(moe_problem, max_tokens_per_expert) F(moe_problem, shared_N) F(moe_problem, global_E)
+  F(moe_problem, chunk_tokens)
   F(moe_problem, format)
   F(moe_problem, apply_router_weight_on_input) F(moe_problem, weight_layout) F(moe_problem, expert_map)
   printf("moe_weights %zu\n", sizeof(moe_weights));
@@ -154,6 +155,11 @@ def test_validation_status_codes():
     p.expert_map = 0x1000
     assert moe.validate(p) == moe.MOE_ERR_UNSUPPORTED
     assert moe.validate(moe.make_problem(**base, global_E=-1)) == moe.MOE_ERR_INVALID_ARG
+    # activation chunking: Standard format only
+    assert moe.validate(moe.make_problem(**base, chunk_tokens=-1)) == moe.MOE_ERR_INVALID_ARG
+    assert moe.validate(moe.make_problem(**base, chunk_tokens=4)) == moe.MOE_OK
+    assert moe.validate(moe.make_problem(**base, chunk_tokens=4, format=moe.FORMAT_BATCHED_EXPERTS,
+                                         max_tokens_per_expert=16)) == moe.MOE_ERR_UNSUPPORTED
     p = moe.make_problem(**base)
     p.scoring = 7
     assert moe.validate(p) == moe.MOE_ERR_INVALID_ARG
@@ -191,7 +197,28 @@ def test_host_errors_need_no_gpu():
     assert L.moe_pack_weights(C.byref(p), C.byref(src), None, fake, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_pack_weights(C.byref(p), C.byref(src), C.c_void_p(0x1000), C.c_void_p(0x3000), None) \
         == moe.MOE_ERR_INVALID_ARG                                                   # in place
+    # chunking belongs to moe_forward: the stage calls refuse a chunked problem
+    pc = moe.make_problem(E=8, M=16, N=256, K=256, topk=2, chunk_tokens=4)
+    wsc = moe.workspace_size(pc)
+    assert L.moe_prepare(C.byref(pc), fake, fake, None, None, None, fake, fake, wsc, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_experts(C.byref(pc), fake, None, C.byref(moe.Weights(0x1000, None, 0x2000, None)), fake, fake,
+                         fake, wsc, None) == moe.MOE_ERR_UNSUPPORTED
     # M == 0: nothing to do, nothing launched
     p0 = moe.make_problem(E=8, M=0, N=256, K=256, topk=2)
     assert L.moe_route(C.byref(p0), None, None, None, None) == moe.MOE_OK
     assert L.moe_forward(C.byref(p0), None, None, None, None, None, None, 0, None, None) == moe.MOE_OK
+
+
+def test_chunked_workspace_holds_one_chunk():
+    wl = WORKLOADS["dsv3_bf16"]
+    full = moe.workspace_layout(_prob(wl))
+    p = _prob(wl)
+    p.chunk_tokens = 512
+    ch = moe.workspace_layout(p)
+    assert ch.perm_len == 512 * wl.topk and ch.act_rows == 512 * wl.topk
+    assert ch.total_bytes < full.total_bytes
+    # the batch-wide regions keep their size: the pair -> slot map (read by the
+    # combine) and the (M, topk, K) expert output
+    assert ch.act - ch.inv == full.act - full.inv
+    assert ch.shared_act - ch.fused_out == full.shared_act - full.fused_out
+    assert moe.validate(p) == moe.MOE_OK

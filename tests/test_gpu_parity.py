@@ -675,3 +675,66 @@ def test_router_weight_on_input_parity(name):
     # the weight is applied once: against the plain layer the output differs
     plain, _, _ = oracle.moe_tokens(wl.replace(router_weight_on_input=False), d, toks)
     assert U.rel_err(plain, ref) > 10 * U.tol_for(wl)
+
+
+# ----------------------------------------------------------------- activation chunking
+
+CHUNK_CASES = {
+    # streaming kernel for the batch and for every chunk: bitwise equal to unchunked
+    "bf16_stream": (WORKLOADS["mixtral_bf16"].replace(M=300, K=384, I=256, E=7, topk=3, renormalize=False,
+                                                      logits_dist="normal"), 128, True),
+    "fp8_standard": (WORKLOADS["decode_fp8_m64"].replace(M=200, K=256, I=256, E=6, topk=3,
+                                                         format=FORMAT_STANDARD, capacity=0), 64, True),
+    "weight_on_input": (WORKLOADS["mixtral_bf16"].replace(M=300, K=384, I=256, E=6, topk=1, renormalize=False,
+                                                          logits_dist="normal", router_weight_on_input=True),
+                        100, True),
+    # MFMA tiles for the batch, weight streaming for each chunk: same result within the bar
+    "bf16_mfma_to_stream": (WORKLOADS["mixtral_bf16"].replace(M=1200, K=256, I=256, E=4, topk=2,
+                                                              renormalize=False, logits_dist="normal"), 500, False),
+}
+
+
+@pytest.mark.parametrize("name", list(CHUNK_CASES))
+def test_chunked_forward(name):
+    """The experts step in chunks of tokens (per-chunk recount, permutation,
+    tile plan and GEMMs): each token's result is unchanged."""
+    wl, chunk, bitwise = CHUNK_CASES[name]
+    dcpu = make_inputs(wl, seed=34, device="cpu")
+    d = U.to_cuda(dcpu)
+    ref, _, _, _ = U.run_forward(wl, d)
+    pc = U.problem(wl, chunk_tokens=chunk)
+    assert moe.workspace_size(pc) < moe.workspace_size(U.problem(wl))
+    got, _, ws, _ = U.run_forward(wl, d, p=pc)
+    torch.cuda.synchronize()
+    L = moe.workspace_layout(pc)
+    assert U.ws_view(ws, L.status, 1).item() == 0
+    if bitwise:
+        assert torch.equal(got, ref)
+    toks = sample_tokens(wl.M, 16, seed=8)
+    oref, _, _ = oracle.moe_tokens(wl, dcpu, toks)
+    err = U.rel_err(got.float().cpu().numpy()[toks], oref)
+    print(f"  chunked {name}: max rel err {err:.3e}", flush=True)
+    assert err <= U.tol_for(wl)
+
+
+def test_chunked_forward_with_shard_map_and_bad_ids_flag():
+    """Chunks of an expert-parallel shard; a bad id in the first chunk stays
+    flagged after the later chunks run."""
+    wl = SHARD_CASES["bf16_standard"]
+    d = make_inputs(wl, seed=35, device="cpu")
+    ds, El = _shard_inputs(d, wl.E, 3, 1)
+    wls = wl.replace(E=El, global_E=wl.E)
+    g = U.to_cuda(ds)
+    ref, _, _, _ = U.run_forward(wls, g)
+    pc = U.problem(wls, expert_map=g["expert_map"], chunk_tokens=64)
+    got, _, _, _ = U.run_forward(wls, g, p=pc)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    # a map entry outside [-1, E) on a picked expert: flagged, and kept across chunks
+    bad_map = g["expert_map"].clone()
+    picked = oracle.route(ds["logits"], wl.topk, wl.scoring, wl.renormalize)[0][0, 0]
+    bad_map[int(picked)] = El + 5
+    pb = U.problem(wls, expert_map=bad_map, chunk_tokens=64)
+    _, _, ws, _ = U.run_forward(wls, g, p=pb)
+    torch.cuda.synchronize()
+    assert U.ws_view(ws, moe.workspace_layout(pb).status, 1).item() & moe.DEVICE_BAD_EXPERT_ID
