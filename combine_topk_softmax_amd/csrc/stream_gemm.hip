@@ -368,6 +368,59 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
         return;
       }
     }
+    if constexpr (OUT_BF16) {
+      // bf16 tiles go through LDS and leave as whole rows of 16-byte stores
+      // (one 2-byte store per element cost a fifth of the down GEMM on the
+      // DeepSeek shapes).  Rows are staged in passes that fit the A buffers;
+      // the 16-byte row padding spreads the 4 rows a store instruction
+      // touches over different banks.
+      constexpr int kCols = GATED ? 128 : 128 * NBW;
+      constexpr int kRowBytes = kCols * 2;
+      constexpr int kPitch = kRowBytes + 16;
+      constexpr int kFit = (2 * TMAX * 128 / kPitch) / 16 * 16;
+      constexpr int RP = kFit < NMB * 16 ? kFit : NMB * 16;
+      constexpr int kChunks = kRowBytes / 16;
+      static_assert(RP >= 16, "staging buffer holds at least one row block");
+      uint8_t *stage = &As[0][0];
+      const int64_t col0 = (int64_t)nt * kCols;
+      __syncthreads();   // every wavefront is done reading the A tiles
+#pragma unroll
+      for (int p0 = 0; p0 < NMB * 16; p0 += RP) {
+#pragma unroll
+        for (int mb = p0 / 16; mb < (p0 + RP) / 16 && mb < NMB; ++mb) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            uint8_t *row = stage + (mb * 16 + q * 4 + i - p0) * kPitch;
+            if constexpr (GATED) {
+              const float v = gated_act(acc[mb][0][i], acc[mb][1][i], g.act);
+              *reinterpret_cast<uint16_t *>(row + (wv * 16 + r16) * 2) = f32_to_bf16_bits(v);
+            } else {
+#pragma unroll
+              for (int b = 0; b < NBW; ++b)
+                *reinterpret_cast<uint16_t *>(row + (wv * 16 * NBW + b * 16 + r16) * 2) =
+                    f32_to_bf16_bits(acc[mb][b][i]);
+            }
+          }
+        }
+        __syncthreads();
+        const int nrows = min(RP, T - p0);
+        for (int c = tid; c < nrows * kChunks; c += kThreads) {
+          const int rl = c / kChunks, off = (c - rl * kChunks) * 16;
+          const int64_t slot = row0 + p0 + rl;
+          int64_t orow = slot;
+          if constexpr (!GATED) {
+            if (g.out_perm) {
+              orow = g.out_perm[slot];
+              if (orow < 0 || orow >= g.n_pairs) continue;
+            }
+          }
+          *reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(g.out) + (orow * g.ldo + col0) * 2 + off) =
+              *reinterpret_cast<const u32x4 *>(stage + rl * kPitch + off);
+        }
+        __syncthreads();
+      }
+      return;
+    }
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
