@@ -207,29 +207,45 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const GemmParams g,
   }
 
   // Epilogue.  Accumulator element i of a 32x32 block sits at column
-  // (lane % 32) and row 8 (i / 4) + 4 (lane / 32) + i % 4.
+  // (lane % 32) and row 8 (i / 4) + 4 (lane / 32) + i % 4.  The bf16 tile is
+  // staged in LDS (rows 0-127 in the A buffers, 128-255 in the B buffers) and
+  // leaves as whole rows of 16-byte stores; the 16-byte row padding puts the
+  // two rows of each 2-byte store instruction on different banks.
+  constexpr int kOutCols = GATED ? 128 : kCols;
+  constexpr int kRowB = kOutCols * 2, kSP = kRowB + 16, kChunk = kRowB / 16;
+  static_assert(128 * kSP <= 2 * kRows * kPitch, "half a tile fits each operand's LDS buffers");
+  __syncthreads();   // every wavefront is done reading the operand tiles
+  uint8_t *half = wm == 0 ? &As[0][0] : &Bs[0][0];   // rows wm*128 .. +128
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int r = wm * 128 + mb * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-      if (r >= T) continue;
-      const int64_t slot = row0 + r;
+      uint8_t *row = half + (mb * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3)) * kSP;
       if constexpr (GATED) {
-        const float gt = acc[mb][0][i], up = acc[mb][1][i];
-        const float v = gated_act(gt, up, g.act);
-        const int64_t col = (int64_t)nt * 128 + wn * 32 + (lane & 31);
-        reinterpret_cast<uint16_t *>(g.out)[slot * g.ldo + col] = f32_to_bf16_bits(v);
+        const float v = gated_act(acc[mb][0][i], acc[mb][1][i], g.act);
+        *reinterpret_cast<uint16_t *>(row + (wn * 32 + (lane & 31)) * 2) = f32_to_bf16_bits(v);
       } else {
-        const int64_t orow = g.out_perm ? g.out_perm[slot] : slot;
-        if (orow < 0 || (g.out_perm && orow >= g.n_pairs)) continue;
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const int64_t col = (int64_t)nt * kCols + wn * 64 + nb * 32 + (lane & 31);
-          reinterpret_cast<uint16_t *>(g.out)[orow * g.ldo + col] = f32_to_bf16_bits(acc[mb][nb][i]);
-        }
+        for (int nb = 0; nb < 2; ++nb)
+          *reinterpret_cast<uint16_t *>(row + (wn * 64 + nb * 32 + (lane & 31)) * 2) = f32_to_bf16_bits(acc[mb][nb][i]);
       }
     }
+  }
+  __syncthreads();
+  const int64_t col0 = (int64_t)nt * kOutCols;
+  for (int c = tid; c < T * kChunk; c += kThreads) {
+    const int r = c / kChunk, off = (c - r * kChunk) * 16;
+    const int64_t slot = row0 + r;
+    int64_t orow = slot;
+    if constexpr (!GATED) {
+      if (g.out_perm) {
+        orow = g.out_perm[slot];
+        if (orow < 0 || orow >= g.n_pairs) continue;
+      }
+    }
+    const uint8_t *src = (r < 128 ? &As[0][0] : &Bs[0][0]) + (r & 127) * kSP + off;
+    *reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(g.out) + (orow * g.ldo + col0) * 2 + off) =
+        *reinterpret_cast<const u32x4 *>(src);
   }
 }
 
