@@ -242,7 +242,9 @@ def main():
         # the stage events mark the last chunk's kernels only: no per-launch roofline
         roofline = {"bound": None, "note": "chunked run: stage events cover the last chunk only"}
     result = {
-        "metric": "MoE layer tokens/s (grouped-GEMM roofline fraction reported alongside), 1 GPU",
+        # value is the layer's tokens/s; the grouped GEMMs' TFLOP/s and roofline
+        # fraction are in gemm_tflops and roofline
+        "metric": "MoE layer tokens/s and grouped-GEMM TFLOP/s (% MFMA or HBM roofline), 1 GPU",
         "value": wl.M / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
