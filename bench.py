@@ -124,8 +124,8 @@ def copy_calibration(gib: float):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              f"(the multi-GPU expert-parallel design is described, not built)", flush=True)
+        print(f"bench.py: the fused MoE layer here runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(there is no multi-GPU expert-parallel path)", flush=True)
         sys.exit(2)
     import numpy as np
     import torch
