@@ -514,6 +514,16 @@ MUTANTS = [
     ("weighted bf16 input not rounded to bf16", "return act_dtype == OR_BF16 ? (double)round_bf16(p) : (double)p;",
      "return (double)p;",
      [lambda: test_router_weight_on_input_matches_brute_force(oracle.BF16)]),
+    ("fp8 weight block scales read transposed", "scale[(e * (R / 128) + r / 128) * (C / 128) + c / 128]",
+     "scale[(e * (C / 128) + c / 128) * (R / 128) + r / 128]",
+     [test_fp8_layer_matches_dense_brute_force]),
+    ("act not re-quantised before the down GEMM", "  if (requant_fp8) {\n", "  if (0) {\n",
+     [test_fp8_layer_matches_dense_brute_force]),
+    ("batched capacity check off by one", "inv[f] = r < cap ? (int32_t)(e * cap + r) : -1;",
+     "inv[f] = r <= cap ? (int32_t)(e * cap + r) : -1;",
+     [lambda: test_batched_slots(5)]),
+    ("group maximum taken over signed values", "float a = fabsf(xg[i]);", "float a = xg[i];",
+     [test_quant_g128_matches_torch_and_bounds]),
 ]
 
 
