@@ -738,3 +738,48 @@ def test_chunked_forward_with_shard_map_and_bad_ids_flag():
     _, _, ws, _ = U.run_forward(wls, g, p=pb)
     torch.cuda.synchronize()
     assert U.ws_view(ws, moe.workspace_layout(pb).status, 1).item() & moe.DEVICE_BAD_EXPERT_ID
+
+
+# ------------------------------------------------------- random shapes
+
+def _random_cases(n=24, seed=2024):
+    """Seeded random small layers over dtype, format, scoring, activation and
+    ragged sizes, so that every grouped-GEMM kernel (weight streaming, 256x256
+    MFMA tiles, 128x128 tiles) meets shapes the named cases do not."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        kind = ["f32", "bf16", "bf16", "fp8"][int(rng.integers(4))]
+        E = int(rng.integers(1, 41))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        M = int(rng.integers(1, 400))
+        K = 128 * int(rng.integers(1, 7))
+        I = (128 if kind == "fp8" else 64) * int(rng.integers(1, 7))
+        if M * k * I * K > 2e8:
+            continue
+        batched = kind != "f32" and rng.random() < 0.4
+        base = dict(tiny_fp32="tiny_fp32", bf16="mixtral_bf16", fp8="decode_fp8_m64")
+        wl = WORKLOADS[base.get(kind, "tiny_fp32")].replace(
+            M=M, K=K, I=I, E=E, topk=k, logits_dist="normal",
+            scoring=SCORING_SIGMOID if rng.random() < 0.3 else 0,
+            renormalize=bool(rng.random() < 0.5), activation=int(rng.random() < 0.3),
+            format=FORMAT_BATCHED if (batched or kind == "fp8") else FORMAT_STANDARD,
+            capacity=M if (batched or kind == "fp8") else 0)
+        cases.append((f"{kind}_E{E}_k{k}_M{M}_K{K}_I{I}_{'bat' if wl.format else 'std'}", wl))
+    return cases
+
+
+RANDOM_CASES = _random_cases()
+
+
+@pytest.mark.parametrize("name,wl", RANDOM_CASES, ids=[c[0] for c in RANDOM_CASES])
+def test_forward_random_shapes(name, wl):
+    d = make_inputs(wl, seed=21, device="cpu")
+    out, _, ws, p = U.run_forward(wl, U.to_cuda(d))
+    torch.cuda.synchronize()
+    L = moe.workspace_layout(p)
+    assert int(U.ws_view(ws, L.status, 1).cpu()[0]) == 0
+    ref, _, _ = oracle.moe_tokens(wl, d)
+    err = U.rel_err(out.float().cpu().numpy(), ref)
+    print(f"  {name}: max rel err {err:.3e}", flush=True)
+    assert err <= U.tol_for(wl)
