@@ -44,6 +44,14 @@ def parse():
                     help="expert weight layout (packed once before timing, as at model load)")
     ap.add_argument("--chunk-tokens", type=int, default=0,
                     help="run the experts step in chunks of this many tokens (Standard format; 0 = whole batch)")
+    ap.add_argument("--activation", choices=["silu", "gelu"], default="silu",
+                    help="gated activation of the experts (gelu_and_mul: exact GELU)")
+    ap.add_argument("--router-weight-on-input", action="store_true",
+                    help="top-1 routing with the router weight applied to the input before dispatch")
+    ap.add_argument("--expert-shards", type=int, default=1,
+                    help="run one expert-parallel shard of this many (expert_map: global expert g is local "
+                         "to shard g %% N); routing stays global")
+    ap.add_argument("--shard", type=int, default=0, help="which shard with --expert-shards")
     ap.add_argument("--copy-calibration", type=float, default=0.0,
                     help="only run a plain device copy of this many GiB (counter calibration)")
     return ap.parse_args()
@@ -59,18 +67,21 @@ def kernel_source_hash() -> str:
 
 def gemm1_algorithmic(wl, counts):
     """Bytes and flops of one gated-GEMM launch: the w1 panels of experts that
-    receive tokens, x read once, act written once; 2*rows*2I*K flops."""
+    receive tokens, x read once, act written once; 2*rows*2I*K flops, rows the
+    (token, pick) pairs routed to this GPU's experts (M*topk unsharded)."""
     import numpy as np
     eb_w = {0: 4, 1: 2, 2: 1}[wl.w_dtype]
     eb_a = 4 if wl.act_dtype == 0 else 2
-    active = int((np.asarray(counts) > 0).sum())
+    counts = np.asarray(counts)
+    active = int((counts > 0).sum())
+    rows = int(counts.sum())
     w_bytes = active * 2 * wl.I * wl.K * eb_w
     if wl.w_dtype == 2:
         w_bytes += active * (2 * wl.I // 128) * (wl.K // 128) * 4
     x_bytes = wl.M * wl.K * eb_a
     # act is written once: bf16 / fp32, or (fp8) e4m3 codes plus one fp32 scale per 128 columns
-    act_bytes = wl.M * wl.topk * (wl.I + wl.I // 128 * 4 if wl.w_dtype == 2 else wl.I * eb_a)
-    flops = 2 * wl.M * wl.topk * 2 * wl.I * wl.K
+    act_bytes = rows * (wl.I + wl.I // 128 * 4 if wl.w_dtype == 2 else wl.I * eb_a)
+    flops = 2 * rows * 2 * wl.I * wl.K
     return w_bytes + x_bytes + act_bytes, flops
 
 
@@ -138,15 +149,44 @@ def main():
     from workloads import WORKLOADS, make_inputs
 
     wl = WORKLOADS[args.workload]
+    variant = {}
+    if args.activation == "gelu":
+        wl = wl.replace(activation=moe.ACTIVATION_GELU)
+        variant["activation"] = "gelu"
+    if args.router_weight_on_input:
+        wl = wl.replace(topk=1, renormalize=False, router_weight_on_input=True)
+        variant["router_weight_on_input"] = True
     torch.cuda.set_device(0)
     print(f"[bench] generating inputs for {wl.name}", file=sys.stderr, flush=True)
     d = make_inputs(wl, seed=0, device="cuda")
+    if args.expert_shards > 1:
+        # this GPU's share: global experts g with g % N == shard, local index g // N
+        n, s = args.expert_shards, args.shard
+        if not 0 <= s < n or wl.E % n:
+            print("bench.py: --expert-shards needs 0 <= shard < N and N dividing E", flush=True)
+            sys.exit(2)
+        # the shard runs the routed experts only: a shared expert belongs to
+        # each GPU's own tokens, not to an expert shard
+        wl = wl.replace(shared_I=0)
+        d.pop("w1s", None)
+        d.pop("w2s", None)
+        glob = torch.arange(s, wl.E, n, device="cuda")
+        emap = torch.full((wl.E,), -1, dtype=torch.int32, device="cuda")
+        emap[glob] = torch.arange(glob.numel(), dtype=torch.int32, device="cuda")
+        for k in ("w1", "w2", "w1_scale", "w2_scale"):
+            if d.get(k) is not None:
+                d[k] = d[k][glob].contiguous()
+        d["expert_map"] = emap
+        variant["expert_shard"] = f"{s} of {n} ({glob.numel()} of {wl.E} experts)"
+        wl = wl.replace(E=glob.numel(), global_E=wl.E)
     packed = args.weights == "packed" and wl.I % 128 == 0
     p = moe.make_problem(wl.E, wl.M, 2 * wl.I, wl.K, wl.topk, format=wl.format, act_dtype=wl.act_dtype,
                          w_dtype=wl.w_dtype, act_quant=wl.act_quant, scoring=wl.scoring,
                          renormalize=wl.renormalize, max_tokens_per_expert=wl.capacity, shared_N=2 * wl.shared_I,
                          weight_layout=moe.WEIGHTS_PACKED if packed else moe.WEIGHTS_ROW_MAJOR,
-                         chunk_tokens=args.chunk_tokens)
+                         chunk_tokens=args.chunk_tokens, activation=wl.activation,
+                         apply_router_weight_on_input=wl.router_weight_on_input, global_E=wl.global_E,
+                         expert_map=d.get("expert_map"))
     pack_ms = None
     gw = {"w1": d["w1"], "w2": d["w2"]}
     if packed:
@@ -192,11 +232,15 @@ def main():
     gemm1_ms = float(stage_avg[2])
 
     counts = ws[L.counts: L.counts + 4 * wl.E].view(torch.int32).cpu().numpy()
-    streaming = wl.w_dtype != 0 and wl.M * wl.topk <= wl.E * (128 if wl.w_dtype == 2 else 256)
+    local_pairs = wl.M * wl.topk * wl.E // wl.global_E if wl.global_E > wl.E else wl.M * wl.topk
+    streaming = wl.w_dtype != 0 and local_pairs <= wl.E * (128 if wl.w_dtype == 2 else 256)
     g1_bytes, g1_flops = gemm1_algorithmic(wl, counts)
     achieved = g1_bytes / (gemm1_ms * 1e-3) / 1e9
-    traffic = measured_traffic(wl.name)
-    all_flops = wl.gemm_flops() + wl.shared_flops()
+    # the committed counter summaries cover the plain workloads only
+    traffic = None if variant else measured_traffic(wl.name)
+    rows = int(np.asarray(counts).sum())
+    routed_flops = 2 * rows * 3 * wl.I * wl.K
+    all_flops = routed_flops + wl.shared_flops()
 
     graph_ms = None
     if args.graph:
@@ -260,12 +304,12 @@ def main():
                    "topk": wl.topk, "format": "batched_experts" if wl.format else "standard",
                    "shared_expert_intermediate": wl.shared_I or None,
                    "weight_layout": "packed (one-time reorder before timing)" if packed else "row_major",
-                   "chunk_tokens": args.chunk_tokens or None,
+                   "chunk_tokens": args.chunk_tokens or None, **variant,
                    "workspace_bytes": moe.workspace_size(p)},
         "weight_pack_ms": pack_ms,
         "roofline": roofline,
         "gemm_tflops": {"gated_gemm": g1_flops / (gemm1_ms * 1e-3) / 1e12,
-                        "both_gemms": wl.gemm_flops() / ((stage_avg[2] + stage_avg[3]) * 1e-3) / 1e12,
+                        "both_gemms": routed_flops / ((stage_avg[2] + stage_avg[3]) * 1e-3) / 1e12,
                         "peak": MFMA_PEAK_TFLOPS[dtn]},
         "layer_tflops": all_flops / (ms_per_step * 1e-3) / 1e12,
         "stage_ms": {"route": stage_avg[0], "prepare+plan": stage_avg[1], "gated_gemm": stage_avg[2],

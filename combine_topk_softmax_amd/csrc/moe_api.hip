@@ -198,8 +198,10 @@ moe_status do_experts(const moe_problem &p, const void *a, const float *a_scale,
   int32_t *perm = standard ? at<int32_t>(ws, L.perm) : nullptr;
   // Weight streaming while the average expert holds no more rows than one
   // streaming tile (weights then dominate the bytes); MFMA tiles otherwise.
+  // An expert-parallel shard expects its share E / global_E of the picks.
+  const int64_t local_pairs = p.global_E > p.E ? p.M * p.topk * p.E / p.global_E : p.M * p.topk;
   const bool streaming = p.w_dtype != MOE_DTYPE_F32 && stream_gemm_fits(p.w_dtype, p.K, I) &&
-                         p.M * p.topk <= p.E * (int64_t)stream_gemm_tile_rows(p.w_dtype);
+                         local_pairs <= p.E * (int64_t)stream_gemm_tile_rows(p.w_dtype);
   // Past that point the GEMMs are bound by the matrix cores: 256 x 256 tiles
   // where the shapes allow, the general 128 x 128 kernel otherwise.
   const bool big = !streaming && mfma_gemm_fits(p.w_dtype, p.act_dtype, p.K, I);
