@@ -91,7 +91,7 @@ void layout(const moe_problem &p, moe_ws_layout &L) {
   L.n_chunks = std::max<int64_t>(1, (nc + L.chunk - 1) / L.chunk);
   L.tile_rows = kTileRows;
   const int64_t tiled_rows = standard ? nc : std::min(n, E * cap);
-  L.max_tiles = std::max<int64_t>(1, (tiled_rows + E * (kTileRows - 1)) / kTileRows);
+  L.max_tiles = std::max<int64_t>(1, (tiled_rows + E * (kMinPlanTileRows - 1)) / kMinPlanTileRows);
   L.act_rows = standard ? L.perm_len : E * cap;
 
   int64_t off = 0;
@@ -205,7 +205,11 @@ moe_status do_experts(const moe_problem &p, const void *a, const float *a_scale,
   // Past that point the GEMMs are bound by the matrix cores: 256 x 256 tiles
   // where the shapes allow, the general 128 x 128 kernel otherwise.
   const bool big = !streaming && mfma_gemm_fits(p.w_dtype, p.act_dtype, p.K, I);
-  const int tile_rows = streaming ? stream_gemm_tile_rows(p.w_dtype) : big ? mfma_gemm_tile_rows() : (int)L.tile_rows;
+  const bool wide = streaming && stream_gemm_gated_wide(p.w_dtype, p.E, local_pairs, p.K, I);
+  const int tile_rows = wide        ? stream_gemm_wide_tile_rows()
+                        : streaming ? stream_gemm_tile_rows(p.w_dtype)
+                        : big       ? mfma_gemm_tile_rows()
+                                    : (int)L.tile_rows;
   MOE_HIP(launch_plan_tiles(p, counts, at<int32_t>(ws, L.offsets), L.perm_len, tile_rows,
                             (int)L.max_tiles, tiles, status, s));
   record(ev, 2, s);
@@ -237,9 +241,10 @@ moe_status do_experts(const moe_problem &p, const void *a, const float *a_scale,
     g1.out = at<void>(ws, L.act_q);
     g1.out_scale = at<float>(ws, L.act_scale);
   }
-  if (streaming)
-    MOE_HIP(launch_stream_gemm(p.w_dtype, fp8 ? MOE_DTYPE_F32 : p.act_dtype, kGemmGatedAct, g1,
-                               (int)(I / 128), 1, s));
+  if (streaming) {
+    MOE_HIP(launch_stream_gemm(p.w_dtype, fp8 ? MOE_DTYPE_F32 : p.act_dtype, kGemmGatedAct, g1, (int)(I / 128),
+                               wide ? 4 : 2, s));
+  }
   else if (big)
     MOE_HIP(launch_mfma_gemm(kGemmGatedAct, g1, mfma_gemm_n_tiles(kGemmGatedAct, g1.Nw), s));
   else

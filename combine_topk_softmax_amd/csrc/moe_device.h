@@ -217,8 +217,14 @@ bool stream_gemm_fits(int w_dtype, int64_t K, int64_t I);
 // 16-row weight blocks per wavefront for the down GEMM (1 or 2), from the
 // problem's shape: two when that still leaves enough work items.
 int stream_gemm_down_blocks(int w_dtype, int64_t E, int64_t pairs, int64_t K, int64_t I);
+// Whether the gated GEMM takes wide panels (fp8: 256 act columns per work
+// item, 2 gate + 2 up weight blocks per wavefront); launched with blocks = 4.
+bool stream_gemm_gated_wide(int w_dtype, int64_t E, int64_t pairs, int64_t K, int64_t I);
+int stream_gemm_wide_tile_rows();   // row tiles of the plan when the gated GEMM is wide
+// blocks: gated GEMM 2, or 4 for wide panels; down GEMM weight blocks per
+// wavefront (1 or 2).
 hipError_t launch_stream_gemm(int w_dtype, int out_dtype, GemmKind kind, const GemmParams &g, int n_tiles,
-                              int down_blocks, hipStream_t s);
+                              int blocks, hipStream_t s);
 // Compute-bound variant (bf16, many rows per expert): 256-row tiles; gated
 // tiles cover 128 act columns, down tiles 256 output columns.
 int mfma_gemm_tile_rows();
@@ -234,6 +240,7 @@ hipError_t launch_combine(const moe_problem &p, const void *fused_out, const flo
                           const int32_t *inv, bool rows_from_inv, void *out, hipStream_t s);
 
 constexpr int kTileRows = 128;   // grouped-GEMM rows per tile (BM)
+constexpr int kMinPlanTileRows = 96;   // the smallest row tile any GEMM's plan uses (wide fp8 panels)
 constexpr int kTileCols = 128;   // grouped-GEMM weight rows per tile (BN)
 
 }  // namespace moe

@@ -128,7 +128,9 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
   constexpr bool kScaled = EB == 1;
   constexpr int kFrag = 32 / MM::kSteps;    // bytes per lane per MFMA step
   constexpr int U = D % 2 == 0 ? D : 2 * D; // unroll = lcm(2, D); the host checks nk % U == 0
-  static_assert(!GATED || NBW == 2, "a gated wave holds one gate and one up block");
+  // gated: a wavefront holds GB gate blocks and the GB matching up blocks
+  static_assert(!GATED || NBW == 2 || NBW == 4, "gated: 1 or 2 gate blocks per wavefront");
+  constexpr int GB = GATED ? NBW / 2 : 1;
   static_assert(TMAX % 64 == 0 && TMAX <= 256, "row tile");
 
   __shared__ __attribute__((aligned(16))) uint8_t As[2][TMAX * 128];
@@ -161,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
   for (int b = 0; b < NBW; ++b) {
     int64_t wrow0;
     if (GATED)
-      wrow0 = (b ? g.half_n : 0) + (int64_t)nt * 128 + wv * 16;
+      wrow0 = (b >= GB ? g.half_n : 0) + (int64_t)nt * 128 * GB + wv * 16 * GB + (b % GB) * 16;
     else
       wrow0 = (int64_t)nt * (128 * NBW) + wv * (16 * NBW) + b * 16;
     if (PACKED)
@@ -183,30 +185,39 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
   const int ach = tid & 7;
   const uint8_t *abase = reinterpret_cast<const uint8_t *>(g.a) + ach * 16;
 
-  // Gated fp8: the act tile's 128 columns are exactly one quantisation group,
-  // so the epilogue quantises it directly (the per-token-group e4m3 scheme
-  // that the layer applies to its input, applied again to act before the down
-  // GEMM): row maxima are reduced across the 16 lanes holding a row's columns
-  // in a wavefront, then across the 8 wavefronts through LDS; the codes are
-  // staged in LDS and written as whole 128-byte rows.
-  auto quant_epilogue = [&]<int NMB>(f32x4 (&acc)[NMB][2]) {
+  // Gated fp8: the item's act columns are whole quantisation groups of 128
+  // (one, or two with wide panels), so the epilogue quantises them directly
+  // (the per-token-group e4m3 scheme that the layer applies to its input,
+  // applied again to act before the down GEMM): row maxima are reduced across
+  // the 16 lanes holding a row's columns in a wavefront, then across the
+  // wavefronts of the group through LDS; the codes are staged in LDS and
+  // written as whole rows.
+  auto quant_epilogue = [&]<int NMB>(f32x4 (&acc)[NMB][NBW]) {
+    constexpr int kGroupWaves = 8 / GB;   // wavefronts whose columns form one group
+    constexpr int kRowCodes = 128 * GB;   // code bytes per row of the item
+    static_assert(NMB * 16 * kRowCodes <= 2 * TMAX * 128, "the codes fit the A buffers");
     __syncthreads();   // every wavefront is done reading the A tiles
     float *rmax = reinterpret_cast<float *>(&As[0][0]);   // [TMAX][8]
-    uint8_t *codes = &As[1][0];                           // [TMAX][128]
-    float v[NMB][4];
+    uint8_t *codes = &As[0][0];                           // [TMAX][kRowCodes], once rmax is read
+    const int grp = wv / kGroupWaves;
+    float v[NMB][GB][4];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float gt = acc[mb][0][i], up = acc[mb][1][i];
-        v[mb][i] = gated_act(gt, up, g.act);
-        float m = fabsf(v[mb][i]);
+        float m = 0.0f;
+#pragma unroll
+        for (int gb = 0; gb < GB; ++gb) {
+          v[mb][gb][i] = gated_act(acc[mb][gb][i], acc[mb][gb + GB][i], g.act);
+          m = fmaxf(m, fabsf(v[mb][gb][i]));
+        }
 #pragma unroll
         for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
         if (r16 == 0) rmax[(mb * 16 + q * 4 + i) * 8 + wv] = m;
       }
     }
     __syncthreads();
+    float sc[NMB][4];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
@@ -214,19 +225,29 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
         const int r = mb * 16 + q * 4 + i;
         float amax = 0.0f;
 #pragma unroll
-        for (int w = 0; w < 8; ++w) amax = fmaxf(amax, rmax[r * 8 + w]);
-        const float sc = group_scale(amax);
-        codes[r * 128 + wv * 16 + r16] = (uint8_t)quant_e4m3(v[mb][i], sc);
-        if (wv == 0 && r16 == 0 && r < T) g.out_scale[(row0 + r) * (g.ldo / 128) + nt] = sc;
+        for (int w = 0; w < kGroupWaves; ++w) amax = fmaxf(amax, rmax[r * 8 + grp * kGroupWaves + w]);
+        sc[mb][i] = group_scale(amax);
+        if (wv % kGroupWaves == 0 && r16 == 0 && r < T)
+          g.out_scale[(row0 + r) * (g.ldo / 128) + (int64_t)nt * GB + grp] = sc[mb][i];
       }
     }
+    __syncthreads();   // the row maxima are read: their space takes the codes
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int gb = 0; gb < GB; ++gb)
+          codes[(mb * 16 + q * 4 + i) * kRowCodes + wv * 16 * GB + gb * 16 + r16] =
+              (uint8_t)quant_e4m3(v[mb][gb][i], sc[mb][i]);
     __syncthreads();
-    // 8 threads per row, 16 bytes each
-    for (int c = tid; c < NMB * 16 * 8; c += kThreads) {
-      const int r = c >> 3, b = (c & 7) * 16;
+    // kRowCodes / 16 threads per row, 16 bytes each
+    constexpr int kChunksRow = kRowCodes / 16;
+    for (int c = tid; c < NMB * 16 * kChunksRow; c += kThreads) {
+      const int r = c / kChunksRow, b = (c % kChunksRow) * 16;
       if (r < T)
-        *reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(g.out) + (row0 + r) * g.ldo + (int64_t)nt * 128 + b) =
-            *reinterpret_cast<const u32x4 *>(&codes[r * 128 + b]);
+        *reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(g.out) + (row0 + r) * g.ldo + (int64_t)nt * kRowCodes +
+                                   b) = *reinterpret_cast<const u32x4 *>(&codes[r * kRowCodes + b]);
     }
   };
 
@@ -374,7 +395,7 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
       // DeepSeek shapes).  Rows are staged in passes that fit the A buffers;
       // the 16-byte row padding spreads the 4 rows a store instruction
       // touches over different banks.
-      constexpr int kCols = GATED ? 128 : 128 * NBW;
+      constexpr int kCols = GATED ? 128 * GB : 128 * NBW;
       constexpr int kRowBytes = kCols * 2;
       constexpr int kPitch = kRowBytes + 16;
       constexpr int kFit = (2 * TMAX * 128 / kPitch) / 16 * 16;
@@ -392,8 +413,11 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
           for (int i = 0; i < 4; ++i) {
             uint8_t *row = stage + (mb * 16 + q * 4 + i - p0) * kPitch;
             if constexpr (GATED) {
-              const float v = gated_act(acc[mb][0][i], acc[mb][1][i], g.act);
-              *reinterpret_cast<uint16_t *>(row + (wv * 16 + r16) * 2) = f32_to_bf16_bits(v);
+#pragma unroll
+              for (int gb = 0; gb < GB; ++gb) {
+                const float v = gated_act(acc[mb][gb][i], acc[mb][gb + GB][i], g.act);
+                *reinterpret_cast<uint16_t *>(row + (wv * 16 * GB + gb * 16 + r16) * 2) = f32_to_bf16_bits(v);
+              }
             } else {
 #pragma unroll
               for (int b = 0; b < NBW; ++b)
@@ -429,13 +453,15 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
         if (r >= T) continue;
         const int64_t slot = row0 + r;
         if constexpr (GATED) {
-          const float gt = acc[mb][0][i], up = acc[mb][1][i];
-          const float v = gated_act(gt, up, g.act);
-          const int64_t col = (int64_t)nt * 128 + wv * 16 + r16;
-          if constexpr (OUT_BF16)
-            reinterpret_cast<uint16_t *>(g.out)[slot * g.ldo + col] = f32_to_bf16_bits(v);
-          else
-            reinterpret_cast<float *>(g.out)[slot * g.ldo + col] = v;
+#pragma unroll
+          for (int gb = 0; gb < GB; ++gb) {
+            const float v = gated_act(acc[mb][gb][i], acc[mb][gb + GB][i], g.act);
+            const int64_t col = (int64_t)nt * 128 * GB + wv * 16 * GB + gb * 16 + r16;
+            if constexpr (OUT_BF16)
+              reinterpret_cast<uint16_t *>(g.out)[slot * g.ldo + col] = f32_to_bf16_bits(v);
+            else
+              reinterpret_cast<float *>(g.out)[slot * g.ldo + col] = v;
+          }
         } else {
           const int64_t orow = g.out_perm ? g.out_perm[slot] : slot;
           if (orow < 0 || (g.out_perm && orow >= g.n_pairs)) continue;
@@ -460,7 +486,10 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
     case 2: body.template operator()<2>(); break;
     case 4: body.template operator()<4>(); break;
     case 6: body.template operator()<6>(); break;
-    case 8: body.template operator()<8>(); break;
+    case 8:
+      // wide gated panels take tiles of at most kWideTileRows = 96 rows
+      if constexpr (!(GATED && NBW == 4)) body.template operator()<8>();
+      break;
     default:
       if constexpr (TMAX >= 256) {
         switch (nq) {
@@ -541,12 +570,37 @@ int stream_gemm_down_blocks(int w_dtype, int64_t E, int64_t pairs, int64_t K, in
   return K % 256 == 0 && (I * eb / 128) % u2 == 0 && items >= 512 ? 2 : 1;
 }
 
+// Wide gated panels for fp8: each wavefront holds 2 gate + 2 up blocks, so a
+// work item covers 256 act columns (two quantisation groups) and re-reads the
+// expert's activation rows half as often per weight byte; worth it once
+// experts average 32 to 80 rows.  Weights are prefetched one K-step ahead
+// to leave registers for the doubled accumulators.
+#ifndef MOE_STREAM_WIDE_FP8
+#define MOE_STREAM_WIDE_FP8 1
+#endif
+#ifndef MOE_STREAM_WIDE_D_FP8
+#define MOE_STREAM_WIDE_D_FP8 1
+#endif
+bool stream_gemm_gated_wide(int w_dtype, int64_t E, int64_t pairs, int64_t K, int64_t I) {
+  return MOE_STREAM_WIDE_FP8 && w_dtype == MOE_DTYPE_FP8_E4M3 && I % 256 == 0 &&
+         (K / 128) % unroll_of(MOE_STREAM_WIDE_D_FP8) == 0 && pairs >= 32 * E && pairs <= 80 * E;
+}
+
+// Their accumulators fit up to 6 blocks of 16 rows: the tile plan caps tiles
+// at 96 rows (an expert above that takes two tiles).
+int stream_gemm_wide_tile_rows() { return kMinPlanTileRows; }
+
 hipError_t launch_stream_gemm(int w_dtype, int out_dtype, GemmKind kind, const GemmParams &g, int n_tiles,
-                              int down_blocks, hipStream_t s) {
+                              int blocks, hipStream_t s) {
   const bool fp8 = w_dtype == MOE_DTYPE_FP8_E4M3;
-  if (kind == kGemmGatedAct)
-    return fp8 ? launch_cfg<1, true, 2, MOE_STREAM_GATED_D_FP8, 128>(out_dtype, g, n_tiles, s)
-               : launch_cfg<2, true, 2, MOE_STREAM_GATED_D_BF16, 256>(out_dtype, g, n_tiles, s);
+  if (kind == kGemmGatedAct) {
+    // n_tiles = I / 128 from the caller; wide panels (blocks == 4) cover 256 act columns
+    if (fp8)
+      return blocks == 4 ? launch_cfg<1, true, 4, MOE_STREAM_WIDE_D_FP8, 128>(out_dtype, g, n_tiles / 2, s)
+                         : launch_cfg<1, true, 2, MOE_STREAM_GATED_D_FP8, 128>(out_dtype, g, n_tiles, s);
+    return launch_cfg<2, true, 2, MOE_STREAM_GATED_D_BF16, 256>(out_dtype, g, n_tiles, s);
+  }
+  const int down_blocks = blocks;
   // down: n_tiles = K / 128 from the caller, K / 256 with two blocks per wavefront
   if (down_blocks == 2)
     return fp8 ? launch_cfg<1, false, 2, MOE_STREAM_DOWN2_D_FP8, 128>(out_dtype, g, n_tiles / 2, s)

@@ -176,6 +176,13 @@ SMALL = {
     "bf16_down2": WORKLOADS["mixtral_bf16"].replace(M=256, K=2048, I=128, E=64, topk=4, renormalize=False,
                                                     logits_dist="normal"),
     "fp8_batched_down2": WORKLOADS["decode_fp8_m64"].replace(M=96, K=2048, I=256, E=64, topk=4, capacity=96),
+    # fp8 weight streaming with 32-80 rows per expert: wide gated panels (2 gate +
+    # 2 up blocks per wavefront, 256 act columns = two quantisation groups per
+    # item, row tiles of at most 96 rows); the Zipf case puts more than 96 rows
+    # on one expert, which then takes two row tiles
+    "fp8_wide": WORKLOADS["decode_fp8_m64"].replace(M=96, K=256, I=256, E=4, topk=2, capacity=96),
+    "fp8_wide_two_tiles": WORKLOADS["decode_fp8_m64"].replace(M=150, K=256, I=256, E=4, topk=2, capacity=150,
+                                                              logits_dist="zipf"),
     # the same regime with I % 128 != 0: the general 128 x 128 tile kernel
     "bf16_tiled_I192": WORKLOADS["mixtral_bf16"].replace(M=700, K=384, I=192, E=4, topk=2, renormalize=False,
                                                          logits_dist="normal"),
@@ -247,7 +254,7 @@ def test_shared_expert_parity(M, K, Is):
     assert err <= U.tol_for(wl)
 
 
-@pytest.mark.parametrize("name", ["fp8_batched", "fp8_standard"])
+@pytest.mark.parametrize("name", ["fp8_batched", "fp8_standard", "fp8_wide"])
 def test_act_requant_group_invariants(name):
     """fp8: the gated GEMM writes act as e4m3 codes with one scale per row and
     128 columns, the scale being the group's max magnitude / 448.  So every
