@@ -274,7 +274,7 @@ moe_status do_experts(const moe_problem &p, const void *a, const float *a_scale,
   g2.t = gt;
   if (streaming)
     MOE_HIP(launch_stream_gemm(p.w_dtype, p.act_dtype, kGemmDown, g2, (int)(p.K / 128),
-                               stream_gemm_down_blocks(p.w_dtype, p.E, p.M * p.topk, p.K, I), s));
+                               stream_gemm_down_blocks(p.w_dtype, p.E, local_pairs, p.K, I), s));
   else if (big)
     MOE_HIP(launch_mfma_gemm(kGemmDown, g2, mfma_gemm_n_tiles(kGemmDown, g2.Nw), s));
   else

@@ -214,8 +214,9 @@ hipError_t launch_grouped_gemm(int w_dtype, int out_dtype, GemmKind kind, const 
 // columns, down tiles 128 output columns; rows per tile below.
 int stream_gemm_tile_rows(int w_dtype);
 bool stream_gemm_fits(int w_dtype, int64_t K, int64_t I);
-// 16-row weight blocks per wavefront for the down GEMM (1 or 2), from the
-// problem's shape: two when that still leaves enough work items.
+// 16-row weight blocks per wavefront for the down GEMM (1, 2 or, fp8 with
+// wide gated panels, 4), from the problem's shape: two when that still leaves
+// enough work items.
 int stream_gemm_down_blocks(int w_dtype, int64_t E, int64_t pairs, int64_t K, int64_t I);
 // Whether the gated GEMM takes wide panels (fp8: 256 act columns per work
 // item, 2 gate + 2 up weight blocks per wavefront); launched with blocks = 4.

@@ -487,8 +487,9 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
     case 4: body.template operator()<4>(); break;
     case 6: body.template operator()<6>(); break;
     case 8:
-      // wide gated panels take tiles of at most kWideTileRows = 96 rows
-      if constexpr (!(GATED && NBW == 4)) body.template operator()<8>();
+      // four weight blocks per wavefront (wide fp8 panels) take tiles of at
+      // most 96 rows
+      if constexpr (NBW != 4) body.template operator()<8>();
       break;
     default:
       if constexpr (TMAX >= 256) {
@@ -548,6 +549,12 @@ int stream_gemm_tile_rows(int w_dtype) { return w_dtype == MOE_DTYPE_FP8_E4M3 ? 
 #ifndef MOE_STREAM_DOWN2_D_BF16
 #define MOE_STREAM_DOWN2_D_BF16 2
 #endif
+#ifndef MOE_STREAM_DOWN4_FP8
+#define MOE_STREAM_DOWN4_FP8 1
+#endif
+#ifndef MOE_STREAM_DOWN4_D_FP8
+#define MOE_STREAM_DOWN4_D_FP8 1
+#endif
 #ifndef MOE_STREAM_DOWN2_D_FP8
 #define MOE_STREAM_DOWN2_D_FP8 2
 #endif
@@ -560,14 +567,6 @@ bool stream_gemm_fits(int w_dtype, int64_t K, int64_t I) {
   const int ug = unroll_of(fp8 ? MOE_STREAM_GATED_D_FP8 : MOE_STREAM_GATED_D_BF16);
   const int ud = unroll_of(fp8 ? MOE_STREAM_DOWN_D_FP8 : MOE_STREAM_DOWN_D_BF16);
   return I % 128 == 0 && (K * eb / 128) % ug == 0 && (I * eb / 128) % ud == 0;
-}
-
-int stream_gemm_down_blocks(int w_dtype, int64_t E, int64_t pairs, int64_t K, int64_t I) {
-  const bool fp8 = w_dtype == MOE_DTYPE_FP8_E4M3;
-  const int eb = fp8 ? 1 : 2;
-  const int u2 = unroll_of(fp8 ? MOE_STREAM_DOWN2_D_FP8 : MOE_STREAM_DOWN2_D_BF16);
-  const int64_t items = std::min(E, pairs) * (K / 256);   // at most one row tile per expert
-  return K % 256 == 0 && (I * eb / 128) % u2 == 0 && items >= 512 ? 2 : 1;
 }
 
 // Wide gated panels for fp8: each wavefront holds 2 gate + 2 up blocks, so a
@@ -590,6 +589,20 @@ bool stream_gemm_gated_wide(int w_dtype, int64_t E, int64_t pairs, int64_t K, in
 // at 96 rows (an expert above that takes two tiles).
 int stream_gemm_wide_tile_rows() { return kMinPlanTileRows; }
 
+int stream_gemm_down_blocks(int w_dtype, int64_t E, int64_t pairs, int64_t K, int64_t I) {
+  const bool fp8 = w_dtype == MOE_DTYPE_FP8_E4M3;
+  const int eb = fp8 ? 1 : 2;
+  // fp8 with the wide gated panels' row tiles (experts of 32-80 rows): four
+  // blocks, 512 output columns per item, half the activation re-reads
+  if (MOE_STREAM_DOWN4_FP8 && fp8 && K % 512 == 0 && (I / 128) % unroll_of(MOE_STREAM_DOWN4_D_FP8) == 0 &&
+      stream_gemm_gated_wide(w_dtype, E, pairs, K, I))
+    return 4;
+  const int u2 = unroll_of(fp8 ? MOE_STREAM_DOWN2_D_FP8 : MOE_STREAM_DOWN2_D_BF16);
+  const int64_t items = std::min(E, pairs) * (K / 256);   // at most one row tile per expert
+  return K % 256 == 0 && (I * eb / 128) % u2 == 0 && items >= 512 ? 2 : 1;
+}
+
+
 hipError_t launch_stream_gemm(int w_dtype, int out_dtype, GemmKind kind, const GemmParams &g, int n_tiles,
                               int blocks, hipStream_t s) {
   const bool fp8 = w_dtype == MOE_DTYPE_FP8_E4M3;
@@ -601,7 +614,10 @@ hipError_t launch_stream_gemm(int w_dtype, int out_dtype, GemmKind kind, const G
     return launch_cfg<2, true, 2, MOE_STREAM_GATED_D_BF16, 256>(out_dtype, g, n_tiles, s);
   }
   const int down_blocks = blocks;
-  // down: n_tiles = K / 128 from the caller, K / 256 with two blocks per wavefront
+  // down: n_tiles = K / 128 from the caller, K / 256 with two blocks per
+  // wavefront, K / 512 with four (fp8)
+  if (down_blocks == 4 && fp8)
+    return launch_cfg<1, false, 4, MOE_STREAM_DOWN4_D_FP8, 128>(out_dtype, g, n_tiles / 4, s);
   if (down_blocks == 2)
     return fp8 ? launch_cfg<1, false, 2, MOE_STREAM_DOWN2_D_FP8, 128>(out_dtype, g, n_tiles / 2, s)
                : launch_cfg<2, false, 2, MOE_STREAM_DOWN2_D_BF16, 256>(out_dtype, g, n_tiles / 2, s);

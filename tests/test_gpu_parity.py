@@ -183,6 +183,9 @@ SMALL = {
     "fp8_wide": WORKLOADS["decode_fp8_m64"].replace(M=96, K=256, I=256, E=4, topk=2, capacity=96),
     "fp8_wide_two_tiles": WORKLOADS["decode_fp8_m64"].replace(M=150, K=256, I=256, E=4, topk=2, capacity=150,
                                                               logits_dist="zipf"),
+    # the same with K a multiple of 512: the down GEMM also takes four weight
+    # blocks per wavefront (512 output columns per item)
+    "fp8_wide_down4": WORKLOADS["decode_fp8_m64"].replace(M=96, K=512, I=256, E=4, topk=2, capacity=96),
     # the same regime with I % 128 != 0: the general 128 x 128 tile kernel
     "bf16_tiled_I192": WORKLOADS["mixtral_bf16"].replace(M=700, K=384, I=192, E=4, topk=2, renormalize=False,
                                                          logits_dist="normal"),
