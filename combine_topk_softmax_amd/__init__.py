@@ -67,6 +67,7 @@ class WsLayout(C.Structure):
         "total_bytes", "status", "counts", "offsets", "chunk_hist", "tiles", "perm", "inv", "act",
         "act_q", "act_scale", "topk_weights", "topk_ids", "a_q", "a_scale", "fused_out", "shared_act")]
     _fields_ += [(n, C.c_int64) for n in ("perm_len", "n_chunks", "chunk", "max_tiles", "tile_rows", "act_rows")]
+    _fields_ += [("down_partial", C.c_size_t), ("down_split", C.c_int64)]
 
 
 EXPORTS = ("moe_status_str", "moe_version", "moe_validate", "moe_workspace_size", "moe_workspace_layout",

@@ -75,6 +75,26 @@ moe_status validate(const moe_problem *pp) {
 int64_t chunk_of(const moe_problem &p) { return p.chunk_tokens > 0 ? std::min(p.M, p.chunk_tokens) : p.M; }
 bool chunked(const moe_problem &p) { return p.chunk_tokens > 0 && p.chunk_tokens < p.M; }
 
+// Picks an expert-parallel shard expects of `pairs`: its share E / global_E.
+int64_t local_pairs_of(const moe_problem &p, int64_t pairs) {
+  return p.global_E > p.E ? pairs * p.E / p.global_E : pairs;
+}
+
+// Weight streaming while the average expert holds no more rows than one
+// streaming tile (weights then dominate the bytes); MFMA tiles otherwise.
+bool streaming_of(const moe_problem &p, int64_t local_pairs) {
+  const int64_t I = p.N / 2;
+  return p.w_dtype != MOE_DTYPE_F32 && stream_gemm_fits(p.w_dtype, p.K, I) &&
+         local_pairs <= p.E * (int64_t)stream_gemm_tile_rows(p.w_dtype);
+}
+
+// K splits of the down GEMM for an experts call over `pairs` (Standard format).
+int64_t down_split_of(const moe_problem &p, int64_t pairs) {
+  const int64_t lp = local_pairs_of(p, pairs);
+  if (p.format != MOE_FORMAT_STANDARD || !streaming_of(p, lp)) return 1;
+  return stream_gemm_down_split(p.w_dtype, p.E, lp, p.K, p.N / 2);
+}
+
 void layout(const moe_problem &p, moe_ws_layout &L) {
   memset(&L, 0, sizeof(L));
   const int64_t n = p.M * p.topk;        // pairs of the batch
@@ -118,6 +138,8 @@ void layout(const moe_problem &p, moe_ws_layout &L) {
   L.a_scale = take(need_a && fp8 ? a_rows * (p.K / 128) * 4 : 0);
   L.fused_out = take((standard ? n : E * cap) * p.K * eb);
   L.shared_act = take(p.shared_N > 0 ? p.M * (p.shared_N / 2) * eb : 0);
+  L.down_split = down_split_of(p, nc);
+  L.down_partial = take(L.down_split > 1 ? L.down_split * L.perm_len * p.K * 4 : 0);
   L.total_bytes = (size_t)off;
 }
 
@@ -196,12 +218,8 @@ moe_status do_experts(const moe_problem &p, const void *a, const float *a_scale,
   int32_t *tiles = at<int32_t>(ws, L.tiles);
   int32_t *status = at<int32_t>(ws, L.status);
   int32_t *perm = standard ? at<int32_t>(ws, L.perm) : nullptr;
-  // Weight streaming while the average expert holds no more rows than one
-  // streaming tile (weights then dominate the bytes); MFMA tiles otherwise.
-  // An expert-parallel shard expects its share E / global_E of the picks.
-  const int64_t local_pairs = p.global_E > p.E ? p.M * p.topk * p.E / p.global_E : p.M * p.topk;
-  const bool streaming = p.w_dtype != MOE_DTYPE_F32 && stream_gemm_fits(p.w_dtype, p.K, I) &&
-                         local_pairs <= p.E * (int64_t)stream_gemm_tile_rows(p.w_dtype);
+  const int64_t local_pairs = local_pairs_of(p, p.M * p.topk);
+  const bool streaming = streaming_of(p, local_pairs);
   // Past that point the GEMMs are bound by the matrix cores: 256 x 256 tiles
   // where the shapes allow, the general 128 x 128 kernel otherwise.
   const bool big = !streaming && mfma_gemm_fits(p.w_dtype, p.act_dtype, p.K, I);
@@ -272,7 +290,18 @@ moe_status do_experts(const moe_problem &p, const void *a, const float *a_scale,
   g2.half_n = 0;
   g2.w_packed = p.weight_layout == MOE_WEIGHTS_PACKED;
   g2.t = gt;
-  if (streaming)
+  // a split needs the partial-sum buffer the layout reserved for it (a
+  // shorter last chunk may pick a split its layout did not)
+  const int64_t split = down_split_of(p, p.M * p.topk);
+  if (streaming && split > 1 && split == L.down_split) {
+    g2.out = at<void>(ws, L.down_partial);
+    g2.out_perm = nullptr;
+    g2.k_split = (int)split;
+    g2.split_stride = L.perm_len * p.K;
+    MOE_HIP(launch_stream_gemm(p.w_dtype, MOE_DTYPE_F32, kGemmDown, g2, (int)(p.K / 128), 2, s));
+    MOE_HIP(launch_split_reduce(at<float>(ws, L.down_partial), (int)split, g2.split_stride, perm, L.perm_len,
+                                g2.n_pairs, (int)p.K, p.act_dtype, fused_out, s));
+  } else if (streaming)
     MOE_HIP(launch_stream_gemm(p.w_dtype, p.act_dtype, kGemmDown, g2, (int)(p.K / 128),
                                stream_gemm_down_blocks(p.w_dtype, p.E, local_pairs, p.K, I), s));
   else if (big)

@@ -185,6 +185,11 @@ struct GemmParams {
   int64_t half_n;             // gated: I (up rows start here)
   int act;                    // gated: MOE_ACTIVATION_*
   int w_packed;               // weights in MOE_WEIGHTS_PACKED order
+  // streaming down GEMM split over K: work item s of a panel reduces K-steps
+  // [s, s + 1) * nk / k_split and writes fp32 partial sums by slot to
+  // out + s * split_stride (out_perm unused); 0 or 1: no split
+  int k_split;
+  int64_t split_stride;
   GemmTiles t;
 };
 
@@ -218,6 +223,15 @@ bool stream_gemm_fits(int w_dtype, int64_t K, int64_t I);
 // wide gated panels, 4), from the problem's shape: two when that still leaves
 // enough work items.
 int stream_gemm_down_blocks(int w_dtype, int64_t E, int64_t pairs, int64_t K, int64_t I);
+// K splits of the streaming down GEMM (1: none): bf16 shapes whose panels of
+// two weight blocks leave too few work items to fill the chip (few experts,
+// wide K) take two blocks per wavefront and split the reduction instead; the
+// partial sums then go through launch_split_reduce.
+int stream_gemm_down_split(int w_dtype, int64_t E, int64_t pairs, int64_t K, int64_t I);
+// out[perm[slot]] = sum over s of part[s * stride + slot * K] (rows of K
+// values) for the slots whose perm entry is a pair below n_pairs.
+hipError_t launch_split_reduce(const float *part, int S, int64_t stride, const int32_t *perm, int64_t n_slots,
+                               int n_pairs, int K, int out_dtype, void *out, hipStream_t s);
 // Whether the gated GEMM takes wide panels (fp8: 256 act columns per work
 // item, 2 gate + 2 up weight blocks per wavefront); launched with blocks = 4.
 bool stream_gemm_gated_wide(int w_dtype, int64_t E, int64_t pairs, int64_t K, int64_t I);

@@ -142,13 +142,23 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
   const int per = (total + 7) >> 3;
   const int item = xcd * per + local;
   if (local >= per || item >= total) return;
-  const int c = item / n_tiles, nt = item - c * n_tiles;
+  // item -> (row tile c, K split sk, panel nt): the panels of one split are
+  // adjacent, so concurrent items share the split's activation K range
+  const int c = item / n_tiles;
+  const int S = GATED || g.k_split <= 1 ? 1 : g.k_split;
+  const int n_panels = n_tiles / S;
+  const int sk = S > 1 ? (item - c * n_tiles) / n_panels : 0;
+  const int nt = item - c * n_tiles - sk * n_panels;
   const int32_t *tile = g.t.tiles + (int64_t)c * 4;
   const int e = tile[0];
   const int64_t row0 = (int64_t)tile[1] + tile[2];
   const int T = tile[3];
   const int64_t row_bytes = g.Kred * EB;
-  const int nk = (int)(row_bytes / 128);
+  const int nk = (int)(row_bytes / 128) / S;   // K-steps of this item, from k0
+  const int k0 = sk * nk;
+  // partial sums of a K split: fp32 rows by slot, one slice per split
+  void *const out = S > 1 ? static_cast<void *>(reinterpret_cast<float *>(g.out) + sk * g.split_stride) : g.out;
+  const int32_t *const out_perm = S > 1 ? nullptr : g.out_perm;
   const int q = lane >> 4, r16 = lane & 15;
   const int64_t kblocks = g.Kred / 128;
 
@@ -167,10 +177,12 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
     else
       wrow0 = (int64_t)nt * (128 * NBW) + wv * (16 * NBW) + b * 16;
     if (PACKED)
-      wsrc[b] = reinterpret_cast<const uint8_t *>(g.w) + packed_piece(pg, e, wrow0 + r16, 0, 2 * q);
+      wsrc[b] = reinterpret_cast<const uint8_t *>(g.w) + packed_piece(pg, e, wrow0 + r16, 0, 2 * q) +
+                (int64_t)k0 * kstride;
     else
-      wsrc[b] = reinterpret_cast<const uint8_t *>(g.w) + ((int64_t)e * g.Nw + wrow0 + r16) * row_bytes + q * 32;
-    wscale[b] = kScaled ? g.w_scale + ((int64_t)e * (g.Nw / 128) + wrow0 / 128) * kblocks : nullptr;
+      wsrc[b] = reinterpret_cast<const uint8_t *>(g.w) + ((int64_t)e * g.Nw + wrow0 + r16) * row_bytes + q * 32 +
+                (int64_t)k0 * 128;
+    wscale[b] = kScaled ? g.w_scale + ((int64_t)e * (g.Nw / 128) + wrow0 / 128) * kblocks + k0 : nullptr;
   }
   // A row (in the activation tensor) of tile row r.  Rows past the count map
   // to the last real row (so their loads share its cache lines) and padding
@@ -183,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
     return (f < 0 || f >= g.n_pairs) ? 0 : f / g.topk;
   };
   const int ach = tid & 7;
-  const uint8_t *abase = reinterpret_cast<const uint8_t *>(g.a) + ach * 16;
+  const uint8_t *abase = reinterpret_cast<const uint8_t *>(g.a) + ach * 16 + (int64_t)k0 * 128;
 
   // Gated fp8: the item's act columns are whole quantisation groups of 128
   // (one, or two with wide panels), so the epilogue quantises them directly
@@ -266,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
 #pragma unroll
       for (int i = 0; i < kPasses; ++i)
         ra[j][i] = *reinterpret_cast<const u32x4 *>(abase + arow[i] * row_bytes + (int64_t)ks * 128);
-      if constexpr (kScaled) rsa[j] = g.a_scale[srow * kblocks + ks];
+      if constexpr (kScaled) rsa[j] = g.a_scale[srow * kblocks + k0 + ks];
     };
     auto storeA = [&](int j, int st) {
 #pragma unroll
@@ -433,12 +445,12 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
           const int64_t slot = row0 + p0 + rl;
           int64_t orow = slot;
           if constexpr (!GATED) {
-            if (g.out_perm) {
-              orow = g.out_perm[slot];
+            if (out_perm) {
+              orow = out_perm[slot];
               if (orow < 0 || orow >= g.n_pairs) continue;
             }
           }
-          *reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(g.out) + (orow * g.ldo + col0) * 2 + off) =
+          *reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(out) + (orow * g.ldo + col0) * 2 + off) =
               *reinterpret_cast<const u32x4 *>(stage + rl * kPitch + off);
         }
         __syncthreads();
@@ -458,20 +470,20 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
             const float v = gated_act(acc[mb][gb][i], acc[mb][gb + GB][i], g.act);
             const int64_t col = (int64_t)nt * 128 * GB + wv * 16 * GB + gb * 16 + r16;
             if constexpr (OUT_BF16)
-              reinterpret_cast<uint16_t *>(g.out)[slot * g.ldo + col] = f32_to_bf16_bits(v);
+              reinterpret_cast<uint16_t *>(out)[slot * g.ldo + col] = f32_to_bf16_bits(v);
             else
-              reinterpret_cast<float *>(g.out)[slot * g.ldo + col] = v;
+              reinterpret_cast<float *>(out)[slot * g.ldo + col] = v;
           }
         } else {
-          const int64_t orow = g.out_perm ? g.out_perm[slot] : slot;
-          if (orow < 0 || (g.out_perm && orow >= g.n_pairs)) continue;
+          const int64_t orow = out_perm ? out_perm[slot] : slot;
+          if (orow < 0 || (out_perm && orow >= g.n_pairs)) continue;
 #pragma unroll
           for (int b = 0; b < NBW; ++b) {
             const int64_t col = (int64_t)nt * (128 * NBW) + wv * (16 * NBW) + b * 16 + r16;
             if constexpr (OUT_BF16)
-              reinterpret_cast<uint16_t *>(g.out)[orow * g.ldo + col] = f32_to_bf16_bits(acc[mb][b][i]);
+              reinterpret_cast<uint16_t *>(out)[orow * g.ldo + col] = f32_to_bf16_bits(acc[mb][b][i]);
             else
-              reinterpret_cast<float *>(g.out)[orow * g.ldo + col] = acc[mb][b][i];
+              reinterpret_cast<float *>(out)[orow * g.ldo + col] = acc[mb][b][i];
           }
         }
       }
@@ -521,6 +533,38 @@ hipError_t launch_cfg(int out_dtype, const GemmParams &g, int n_tiles, hipStream
       stream_gemm_kernel<EB, GATED, false, NBW, D, TMAX, false><<<grid, block, 0, s>>>(g, n_tiles);
   }
   return hipGetLastError();
+}
+
+// Sum of the K splits of the down GEMM: one block per slot, 8 columns per
+// thread and pass (two 16-byte loads per split), fp32 in split order.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restrict__ part, int S, int64_t stride,
+                                                           const int32_t *__restrict__ perm, int n_pairs, int K,
+                                                           void *__restrict__ out) {
+  const int64_t slot = blockIdx.x;
+  const int pair = perm[slot];
+  if (pair < 0 || pair >= n_pairs) return;   // alignment padding
+  for (int c = threadIdx.x * 8; c < K; c += 256 * 8) {
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int sk = 0; sk < S; ++sk) {
+      const float4 *src = reinterpret_cast<const float4 *>(part + sk * stride + slot * K + c);
+      const float4 a = src[0], b = src[1];
+      acc[0] += a.x, acc[1] += a.y, acc[2] += a.z, acc[3] += a.w;
+      acc[4] += b.x, acc[5] += b.y, acc[6] += b.z, acc[7] += b.w;
+    }
+    if constexpr (OUT_BF16) {
+      uint32_t u[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        u[i] = (uint32_t)f32_to_bf16_bits(acc[2 * i]) | ((uint32_t)f32_to_bf16_bits(acc[2 * i + 1]) << 16);
+      *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out) + (int64_t)pair * K + c) =
+          make_uint4(u[0], u[1], u[2], u[3]);
+    } else {
+      float4 *dst = reinterpret_cast<float4 *>(reinterpret_cast<float *>(out) + (int64_t)pair * K + c);
+      dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+  }
 }
 
 }  // namespace
@@ -602,6 +646,29 @@ int stream_gemm_down_blocks(int w_dtype, int64_t E, int64_t pairs, int64_t K, in
   return K % 256 == 0 && (I * eb / 128) % u2 == 0 && items >= 512 ? 2 : 1;
 }
 
+#ifndef MOE_STREAM_DOWN_SPLIT
+#define MOE_STREAM_DOWN_SPLIT 2
+#endif
+int stream_gemm_down_split(int w_dtype, int64_t E, int64_t pairs, int64_t K, int64_t I) {
+  if (MOE_STREAM_DOWN_SPLIT <= 1 || w_dtype != MOE_DTYPE_BF16 || K % 256 != 0) return 1;
+  if (stream_gemm_down_blocks(w_dtype, E, pairs, K, I) != 1) return 1;
+  const int S = MOE_STREAM_DOWN_SPLIT;
+  const int u2 = unroll_of(MOE_STREAM_DOWN2_D_BF16);
+  // two-block panels of every split: at least one item per compute unit
+  const int64_t items = std::min(E, pairs) * (K / 256) * S;
+  return (I * 2 / 128) % ((int64_t)S * u2) == 0 && items >= 256 ? S : 1;
+}
+
+hipError_t launch_split_reduce(const float *part, int S, int64_t stride, const int32_t *perm, int64_t n_slots,
+                               int n_pairs, int K, int out_dtype, void *out, hipStream_t s) {
+  if (n_slots <= 0) return hipSuccess;
+  dim3 grid((unsigned)n_slots), block(256);
+  if (out_dtype == MOE_DTYPE_BF16)
+    split_reduce_kernel<true><<<grid, block, 0, s>>>(part, S, stride, perm, n_pairs, K, out);
+  else
+    split_reduce_kernel<false><<<grid, block, 0, s>>>(part, S, stride, perm, n_pairs, K, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_stream_gemm(int w_dtype, int out_dtype, GemmKind kind, const GemmParams &g, int n_tiles,
                               int blocks, hipStream_t s) {
@@ -614,6 +681,11 @@ hipError_t launch_stream_gemm(int w_dtype, int out_dtype, GemmKind kind, const G
     return launch_cfg<2, true, 2, MOE_STREAM_GATED_D_BF16, 256>(out_dtype, g, n_tiles, s);
   }
   const int down_blocks = blocks;
+  if (g.k_split > 1) {
+    // K split (bf16): two blocks per wavefront, fp32 partial sums by slot
+    if (fp8 || down_blocks != 2) return hipErrorInvalidValue;
+    return launch_cfg<2, false, 2, MOE_STREAM_DOWN2_D_BF16, 256>(MOE_DTYPE_F32, g, n_tiles / 2 * g.k_split, s);
+  }
   // down: n_tiles = K / 128 from the caller, K / 256 with two blocks per
   // wavefront, K / 512 with four (fp8)
   if (down_blocks == 4 && fp8)

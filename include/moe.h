@@ -188,6 +188,9 @@ typedef struct moe_ws_layout {
   int64_t max_tiles;
   int64_t tile_rows;  /* rows per grouped-GEMM tile                      */
   int64_t act_rows;   /* rows of act (perm_len or E*capacity)            */
+  size_t down_partial;/* fp32[down_split][perm_len][K]: K-split partial   */
+                      /* sums of the down GEMM (empty when not split)     */
+  int64_t down_split; /* K splits of the down GEMM (1: none)              */
 } moe_ws_layout;
 
 const char *moe_status_str(moe_status s);

@@ -222,3 +222,25 @@ def test_chunked_workspace_holds_one_chunk():
     assert ch.act - ch.inv == full.act - full.inv
     assert ch.shared_act - ch.fused_out == full.shared_act - full.fused_out
     assert moe.validate(p) == moe.MOE_OK
+
+
+def test_down_gemm_k_split_layout():
+    # few experts and wide K in bf16 (the Mixtral shape): the streaming down
+    # GEMM splits K in two and the workspace holds both fp32 partial slices
+    wl = WORKLOADS["mixtral_bf16"]
+    L = moe.workspace_layout(_prob(wl))
+    assert L.down_split == 2
+    assert L.down_partial % 256 == 0 and L.down_partial >= L.shared_act
+    assert L.total_bytes >= L.down_partial + 2 * L.perm_len * wl.K * 4
+    # many experts (DeepSeek-V3 shape), fp8 weights, or rows past one
+    # streaming tile: no split and no partial slices
+    for name in ("dsv3_bf16", "decode_fp8_m256", "skewed_bf16"):
+        L = moe.workspace_layout(_prob(WORKLOADS[name]))
+        assert L.down_split == 1 and L.total_bytes <= L.down_partial + 256
+    # a chunked call reserves the split of one chunk
+    p = _prob(wl)
+    p.chunk_tokens = 128
+    ch = moe.workspace_layout(p)
+    assert ch.down_split in (1, 2)
+    if ch.down_split == 2:
+        assert ch.total_bytes >= ch.down_partial + 2 * ch.perm_len * wl.K * 4

@@ -186,6 +186,14 @@ SMALL = {
     # the same with K a multiple of 512: the down GEMM also takes four weight
     # blocks per wavefront (512 output columns per item)
     "fp8_wide_down4": WORKLOADS["decode_fp8_m64"].replace(M=96, K=512, I=256, E=4, topk=2, capacity=96),
+    # bf16 weight streaming with few experts and wide K: two-block down panels
+    # would leave too few work items, so the down GEMM splits K in two and a
+    # reduce sums the fp32 partials into the pair rows; the Zipf case puts
+    # several row tiles on one expert and none on others
+    "bf16_split_k": WORKLOADS["mixtral_bf16"].replace(M=64, K=4096, I=512, E=8, topk=2, renormalize=False,
+                                                      logits_dist="normal"),
+    "bf16_split_k_zipf": WORKLOADS["mixtral_bf16"].replace(M=200, K=4096, I=512, E=8, topk=2,
+                                                           logits_dist="zipf"),
     # the same regime with I % 128 != 0: the general 128 x 128 tile kernel
     "bf16_tiled_I192": WORKLOADS["mixtral_bf16"].replace(M=700, K=384, I=192, E=4, topk=2, renormalize=False,
                                                          logits_dist="normal"),
