@@ -616,8 +616,10 @@ bool stream_gemm_fits(int w_dtype, int64_t K, int64_t I) {
 // Wide gated panels for fp8: each wavefront holds 2 gate + 2 up blocks, so a
 // work item covers 256 act columns (two quantisation groups) and re-reads the
 // expert's activation rows half as often per weight byte; worth it once
-// experts average 32 to 80 rows.  Weights are prefetched one K-step ahead
-// to leave registers for the doubled accumulators.
+// experts average 32 to 80 rows, and while the halved item count still gives
+// every compute unit one (an expert-parallel shard of a few experts keeps
+// the narrow panels).  Weights are prefetched one K-step ahead to leave
+// registers for the doubled accumulators.
 #ifndef MOE_STREAM_WIDE_FP8
 #define MOE_STREAM_WIDE_FP8 1
 #endif
@@ -626,7 +628,8 @@ bool stream_gemm_fits(int w_dtype, int64_t K, int64_t I) {
 #endif
 bool stream_gemm_gated_wide(int w_dtype, int64_t E, int64_t pairs, int64_t K, int64_t I) {
   return MOE_STREAM_WIDE_FP8 && w_dtype == MOE_DTYPE_FP8_E4M3 && I % 256 == 0 &&
-         (K / 128) % unroll_of(MOE_STREAM_WIDE_D_FP8) == 0 && pairs >= 32 * E && pairs <= 80 * E;
+         (K / 128) % unroll_of(MOE_STREAM_WIDE_D_FP8) == 0 && pairs >= 32 * E && pairs <= 80 * E &&
+         E * (I / 256) >= 256;
 }
 
 // Their accumulators fit up to 6 blocks of 16 rows: the tile plan caps tiles

@@ -176,16 +176,20 @@ SMALL = {
     "bf16_down2": WORKLOADS["mixtral_bf16"].replace(M=256, K=2048, I=128, E=64, topk=4, renormalize=False,
                                                     logits_dist="normal"),
     "fp8_batched_down2": WORKLOADS["decode_fp8_m64"].replace(M=96, K=2048, I=256, E=64, topk=4, capacity=96),
-    # fp8 weight streaming with 32-80 rows per expert: wide gated panels (2 gate +
-    # 2 up blocks per wavefront, 256 act columns = two quantisation groups per
-    # item, row tiles of at most 96 rows); the Zipf case puts more than 96 rows
-    # on one expert, which then takes two row tiles
-    "fp8_wide": WORKLOADS["decode_fp8_m64"].replace(M=96, K=256, I=256, E=4, topk=2, capacity=96),
-    "fp8_wide_two_tiles": WORKLOADS["decode_fp8_m64"].replace(M=150, K=256, I=256, E=4, topk=2, capacity=150,
+    # fp8 weight streaming with 32-80 rows per expert and at least 256 wide
+    # items: wide gated panels (2 gate + 2 up blocks per wavefront, 256 act
+    # columns = two quantisation groups per item, row tiles of at most 96
+    # rows); the Zipf case puts more than 96 rows on some experts, which then
+    # take several row tiles
+    "fp8_wide": WORKLOADS["decode_fp8_m64"].replace(M=192, K=256, I=2048, E=32, topk=8, capacity=192),
+    "fp8_wide_two_tiles": WORKLOADS["decode_fp8_m64"].replace(M=300, K=256, I=2048, E=32, topk=8, capacity=300,
                                                               logits_dist="zipf"),
     # the same with K a multiple of 512: the down GEMM also takes four weight
     # blocks per wavefront (512 output columns per item)
-    "fp8_wide_down4": WORKLOADS["decode_fp8_m64"].replace(M=96, K=512, I=256, E=4, topk=2, capacity=96),
+    "fp8_wide_down4": WORKLOADS["decode_fp8_m64"].replace(M=192, K=512, I=2048, E=32, topk=8, capacity=192),
+    # too few experts for a wide item per compute unit (an expert-parallel
+    # shard's share): narrow panels
+    "fp8_few_experts": WORKLOADS["decode_fp8_m64"].replace(M=96, K=256, I=256, E=4, topk=2, capacity=96),
     # bf16 weight streaming with few experts and wide K: two-block down panels
     # would leave too few work items, so the down GEMM splits K in two and a
     # reduce sums the fp32 partials into the pair rows; the Zipf case puts
