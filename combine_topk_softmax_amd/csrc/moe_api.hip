@@ -209,9 +209,37 @@ moe_status do_prepare(const moe_problem &p, const void *x, const int32_t *ids, c
   return do_rows(p, x, topk_w, a_out, a_scale_out, ws, L, s);
 }
 
+// The shared expert's launch on its aux stream, started from the main stream's
+// position at the time of the call.
+struct SharedStart {
+  const moe_problem *p;
+  const void *x;
+  const moe_shared *shared;
+  void *ws;
+  const moe_ws_layout *L;
+};
+
+moe_status do_shared(const moe_problem &p, const void *x, const void *w1, const void *w2, void *out,
+                     void *ws, const moe_ws_layout &L, hipStream_t s);
+
+moe_status start_shared(const SharedStart &sh, hipStream_t main) {
+  MOE_HIP(hipEventRecord(sh.shared->input_ready, main));
+  MOE_HIP(hipStreamWaitEvent(sh.shared->aux_stream, sh.shared->input_ready, 0));
+  const moe_status st = do_shared(*sh.p, sh.x, sh.shared->w1, sh.shared->w2, sh.shared->out, sh.ws, *sh.L,
+                                  sh.shared->aux_stream);
+  if (st != MOE_OK) return st;
+  MOE_HIP(hipEventRecord(sh.shared->output_ready, sh.shared->aux_stream));
+  return MOE_OK;
+}
+
+// sh: start the shared expert once the gated grouped GEMM is queued.  Its
+// GEMMs fill every compute unit: started with the layer, they held the units
+// the short counting and planning kernels waited for (DeepSeek-V3 shape:
+// 0.33 ms instead of 0.04); overlapping the gated GEMM, they slowed it by
+// 0.35 ms; overlapping the down GEMM costs about 0.3 ms and measured best.
 moe_status do_experts(const moe_problem &p, const void *a, const float *a_scale, const moe_weights &w,
                       const int32_t *counts, void *fused_out, void *ws, const moe_ws_layout &L,
-                      hipStream_t s, const moe_stage_events *ev) {
+                      hipStream_t s, const moe_stage_events *ev, const SharedStart *sh = nullptr) {
   const bool standard = p.format == MOE_FORMAT_STANDARD;
   const bool fp8 = fp8_path(p);
   const int64_t I = p.N / 2;
@@ -269,6 +297,10 @@ moe_status do_experts(const moe_problem &p, const void *a, const float *a_scale,
     MOE_HIP(launch_grouped_gemm(p.w_dtype, fp8 ? MOE_DTYPE_F32 : p.act_dtype, kGemmGatedAct, g1,
                                 (int)(I / 64), s));
   record(ev, 3, s);
+  if (sh) {
+    const moe_status st = start_shared(*sh, s);
+    if (st != MOE_OK) return st;
+  }
   if (fp8 && !streaming)
     MOE_HIP(launch_quant_rows(at<float>(ws, L.act), tiles, (int)L.max_tiles, I, at<uint8_t>(ws, L.act_q),
                               at<float>(ws, L.act_scale), s));
@@ -498,14 +530,10 @@ moe_status moe_forward(const moe_problem *p, const float *logits, const void *x,
     if (out == x || shared->out == x) return MOE_ERR_INVALID_ARG;
   }
   record(events, 0, stream);
-  if (shared) {
-    // Shared expert on the aux stream, overlapping the routed path.
-    MOE_HIP(hipEventRecord(shared->input_ready, stream));
-    MOE_HIP(hipStreamWaitEvent(shared->aux_stream, shared->input_ready, 0));
-    if ((st = do_shared(*p, x, shared->w1, shared->w2, shared->out, workspace, L, shared->aux_stream)) != MOE_OK)
-      return st;
-    MOE_HIP(hipEventRecord(shared->output_ready, shared->aux_stream));
-  }
+  // Shared expert on the aux stream, overlapping the routed path: from the
+  // down GEMM on, or from the start when the experts step is chunked.
+  const SharedStart sh{p, x, shared, workspace, &L};
+  if (shared && chunked(*p) && (st = start_shared(sh, stream)) != MOE_OK) return st;
   float *tw = at<float>(workspace, L.topk_weights);
   int32_t *ti = at<int32_t>(workspace, L.topk_ids);
   MOE_HIP(launch_route(*p, logits, tw, ti, stream));
@@ -519,7 +547,8 @@ moe_status moe_forward(const moe_problem *p, const float *logits, const void *x,
   void *fused = at<void>(workspace, L.fused_out);
   if (!chunked(*p)) {
     if ((st = do_prepare(*p, x, ti, tw, a_q, a_s, counts, workspace, L, stream)) != MOE_OK) return st;
-    if ((st = do_experts(*p, a_q ? a_q : x, a_s, *w, counts, fused, workspace, L, stream, events)) != MOE_OK)
+    if ((st = do_experts(*p, a_q ? a_q : x, a_s, *w, counts, fused, workspace, L, stream, events,
+                         shared ? &sh : nullptr)) != MOE_OK)
       return st;
   } else {
     // Prepare the whole batch's rows, then count, permute and run the experts

@@ -139,9 +139,12 @@ typedef struct moe_weights {
 } moe_weights;
 
 /* The shared expert and the streams it overlaps on (SharedExperts page,
- * maybe_forward_async / wait): input_ready is recorded on the main stream,
- * the aux stream waits on it and runs the expert, output_ready is recorded on
- * the aux stream and the main stream waits on it before moe_forward returns.
+ * maybe_forward_async / wait): input_ready is recorded on the main stream
+ * (moe_forward: once the routed gated GEMM is queued, so the expert overlaps
+ * the down GEMM; at the start when the experts step is chunked), the aux
+ * stream waits on it and runs the expert,
+ * output_ready is recorded on the aux stream and the main stream waits on it
+ * before moe_forward returns.
  * w1 [shared_N, K], w2 [K, shared_N/2] in act_dtype; out [M, K] in act_dtype. */
 typedef struct moe_shared {
   const void *w1;
