@@ -739,6 +739,32 @@ def test_chunked_forward(name):
     assert err <= U.tol_for(wl)
 
 
+def test_chunked_forward_split_k_and_short_last_chunk():
+    """Few experts and wide K in bf16: the down GEMM splits K into fp32 partial
+    sums for the batch and for the 64-token chunks, whose workspace reserves
+    the split of one chunk; the last chunk of 3 tokens (6 picks on at most 6
+    experts) is below the split's item count and takes unsplit panels.  Every
+    token is compared with the oracle."""
+    wl = SMALL["bf16_split_k"].replace(M=131)
+    pc = U.problem(wl, chunk_tokens=64)
+    full, ch = moe.workspace_layout(U.problem(wl)), moe.workspace_layout(pc)
+    assert full.down_split == 2 and ch.down_split == 2
+    dcpu = make_inputs(wl, seed=35, device="cpu")
+    d = U.to_cuda(dcpu)
+    ref, _, _, _ = U.run_forward(wl, d)
+    got, _, ws, _ = U.run_forward(wl, d, p=pc)
+    torch.cuda.synchronize()
+    assert U.ws_view(ws, ch.status, 1).item() == 0
+    # the full chunks split K exactly as the whole batch does
+    assert torch.equal(got[:128], ref[:128])
+    toks = np.arange(wl.M)
+    oref, _, _ = oracle.moe_tokens(wl, dcpu, toks)
+    for name, out in (("batch", ref), ("chunked", got)):
+        err = U.rel_err(out.float().cpu().numpy(), oref)
+        print(f"  split-K {name}: max rel err {err:.3e}", flush=True)
+        assert err <= U.tol_for(wl)
+
+
 def test_chunked_forward_with_shard_map_and_bad_ids_flag():
     """Chunks of an expert-parallel shard; a bad id in the first chunk stays
     flagged after the later chunks run."""
