@@ -9,12 +9,19 @@
 // another expert-parallel shard holds, adds nothing.  With the router weight
 // applied on the input the outputs are added unweighted.
 //
-// HBM-bound: one block per token, 16-byte vector loads of each of the k rows,
-// fp32 accumulation in j order, one 16-byte store per 8 outputs.
+// HBM-bound: one block per token, 8 outputs per thread and pass.  The picks
+// go in groups of up to 8: their slots and weights first, then every row's
+// 16-byte loads at once (a dropped pick loads nothing), then the fp32 sums in
+// j order, so a thread keeps up to 8 rows in flight instead of one.  Each
+// expert-output row is read once, so bf16 rows are loaded non-temporally
+// (skewed prefill combine 0.237 -> 0.203 ms, DeepSeek-V3 shape 0.109 -> 0.083).
 #include "moe_device.h"
 
 namespace moe {
 namespace {
+
+constexpr int kGroup = 8;   // picks whose row loads are in flight together
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ y, const float *__restrict__ w,
@@ -23,25 +30,57 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ y, c
   const int m = blockIdx.x;
   for (int c = threadIdx.x * 8; c < K; c += 256 * 8) {
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int j = 0; j < k; ++j) {
-      const int64_t pair = (int64_t)m * k + j;
-      const int64_t slot = inv ? (int64_t)inv[pair] : pair;
-      if (slot < 0) continue;                      // dropped, or another shard's pick
-      const int64_t row = rows_from_inv ? slot : pair;
-      const float wj = w ? w[pair] : 1.0f;
-      if constexpr (sizeof(T) == 2) {
-        const uint4 raw = *reinterpret_cast<const uint4 *>(y + row * K + c);
-        const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
+    for (int j0 = 0; j0 < k; j0 += kGroup) {
+      int64_t row[kGroup];
+      float wj[kGroup];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] += wj * bf16_bits_to_f32(u[i] & 0xffffu);
-          acc[2 * i + 1] += wj * bf16_bits_to_f32(u[i] >> 16);
+      for (int u = 0; u < kGroup; ++u) {
+        row[u] = -1;
+        wj[u] = 0.0f;
+        if (j0 + u < k) {
+          const int64_t pair = (int64_t)m * k + j0 + u;
+          const int64_t slot = inv ? (int64_t)inv[pair] : pair;
+          if (slot >= 0) {                         // else dropped, or another shard's pick
+            row[u] = rows_from_inv ? slot : pair;
+            wj[u] = w ? w[pair] : 1.0f;
+          }
+        }
+      }
+      if constexpr (sizeof(T) == 2) {
+        uint4 raw[kGroup];
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u)
+          raw[u] = row[u] >= 0 ? __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+                                     reinterpret_cast<const u32x4 *>(y + row[u] * K + c)))
+                               : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) {
+          if (row[u] < 0) continue;
+          const uint32_t v[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[2 * i] += wj[u] * bf16_bits_to_f32(v[i] & 0xffffu);
+            acc[2 * i + 1] += wj[u] * bf16_bits_to_f32(v[i] >> 16);
+          }
         }
       } else {
-        const float4 *src = reinterpret_cast<const float4 *>(y + row * K + c);
-        const float4 a = src[0], b = src[1];
-        acc[0] += wj * a.x, acc[1] += wj * a.y, acc[2] += wj * a.z, acc[3] += wj * a.w;
-        acc[4] += wj * b.x, acc[5] += wj * b.y, acc[6] += wj * b.z, acc[7] += wj * b.w;
+        float4 lo[kGroup], hi[kGroup];
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) {
+          if (row[u] >= 0) {
+            const float4 *src = reinterpret_cast<const float4 *>(y + row[u] * K + c);
+            lo[u] = src[0], hi[u] = src[1];
+          } else {
+            lo[u] = hi[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) {
+          if (row[u] < 0) continue;
+          const float a = wj[u];
+          acc[0] += a * lo[u].x, acc[1] += a * lo[u].y, acc[2] += a * lo[u].z, acc[3] += a * lo[u].w;
+          acc[4] += a * hi[u].x, acc[5] += a * hi[u].y, acc[6] += a * hi[u].z, acc[7] += a * hi[u].w;
+        }
       }
     }
     if constexpr (sizeof(T) == 2) {
