@@ -107,7 +107,9 @@ void layout(const moe_problem &p, moe_ws_layout &L) {
   const bool fp8 = fp8_path(p);
 
   L.perm_len = standard ? nc + E * (align - 1) : 0;
-  L.chunk = std::max<int64_t>(1024, round_up((nc + 63) / 64, 256));
+  // pairs per counting chunk: at most 64 chunks, each one wavefront of the
+  // rank kernel, which steps through its chunk 64 pairs at a time
+  L.chunk = std::max<int64_t>(64, round_up((nc + 63) / 64, 64));
   L.n_chunks = std::max<int64_t>(1, (nc + L.chunk - 1) / L.chunk);
   L.tile_rows = kTileRows;
   const int64_t tiled_rows = standard ? nc : std::min(n, E * cap);
