@@ -106,6 +106,10 @@ __device__ __forceinline__ F lds_frag(const uint8_t *A, int row, int off) {
 }
 
 constexpr int kThreads = 512;
+constexpr int kXcdUnits = 32;   // compute units per XCD (256 in 8 XCDs)
+#ifndef MOE_STREAM_SPLIT_TAIL
+#define MOE_STREAM_SPLIT_TAIL 1
+#endif
 #ifndef MOE_STREAM_FRAG_AHEAD
 #define MOE_STREAM_FRAG_AHEAD 2
 #endif
@@ -140,8 +144,21 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
   const int total = *g.t.tile_count * n_tiles;
   const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
   const int per = (total + 7) >> 3;
-  const int item = xcd * per + local;
-  if (local >= per || item >= total) return;
+  // An XCD's items past its last whole round (32 compute units) leave units
+  // idle; when they fill at most half a round after at least one whole round,
+  // each of them becomes two work items over the two halves of its rows,
+  // adjacent so that the pair shares its weight panel through L2.  The
+  // outputs are the same: every row is computed as in the whole item.
+  const int whole = per & ~(kXcdUnits - 1), rem = per - whole;
+  const bool split_tail = MOE_STREAM_SPLIT_TAIL && GATED && EB == 2 && whole > 0 && rem <= kXcdUnits / 2;
+  int li = local, half = -1;
+  if (split_tail && local >= whole) {
+    li = whole + ((local - whole) >> 1);
+    half = (local - whole) & 1;
+  }
+  if (li >= per) return;
+  const int item = xcd * per + li;
+  if (item >= total) return;
   // item -> (row tile c, K split sk, panel nt): the panels of one split are
   // adjacent, so concurrent items share the split's activation K range
   const int c = item / n_tiles;
@@ -151,8 +168,18 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
   const int nt = item - c * n_tiles - sk * n_panels;
   const int32_t *tile = g.t.tiles + (int64_t)c * 4;
   const int e = tile[0];
-  const int64_t row0 = (int64_t)tile[1] + tile[2];
-  const int T = tile[3];
+  int64_t row0 = (int64_t)tile[1] + tile[2];
+  int T = tile[3];
+  if (half >= 0) {
+    const int first = ((T + 1) / 2 + 15) & ~15;   // rows of the first half, whole blocks of 16
+    if (half == 0) {
+      T = min(T, first);
+    } else {
+      row0 += first;
+      T -= first;
+      if (T <= 0) return;
+    }
+  }
   const int64_t row_bytes = g.Kred * EB;
   const int nk = (int)(row_bytes / 128) / S;   // K-steps of this item, from k0
   const int k0 = sk * nk;
@@ -519,7 +546,9 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
 template <int EB, bool GATED, int NBW, int D, int TMAX>
 hipError_t launch_cfg(int out_dtype, const GemmParams &g, int n_tiles, hipStream_t s) {
   const int64_t items = (int64_t)g.t.max_tiles * n_tiles;
-  dim3 grid((unsigned)(((items + 7) / 8) * 8)), block(kThreads);
+  // bf16 gated: room for a split tail (at most half a round more per XCD)
+  const int64_t extra = MOE_STREAM_SPLIT_TAIL && GATED && EB == 2 ? 8 * (kXcdUnits / 2) : 0;
+  dim3 grid((unsigned)(((items + 7) / 8) * 8 + extra)), block(kThreads);
   const bool bf = out_dtype == MOE_DTYPE_BF16;
   if (g.w_packed) {
     if (bf)

@@ -198,6 +198,10 @@ SMALL = {
                                                       logits_dist="normal"),
     "bf16_split_k_zipf": WORKLOADS["mixtral_bf16"].replace(M=200, K=4096, I=512, E=8, topk=2,
                                                            logits_dist="zipf"),
+    # bf16 weight streaming with 36 column panels per expert (288 items: one
+    # whole round per XCD plus 4 items, which run as two row halves each)
+    "bf16_split_tail": WORKLOADS["mixtral_bf16"].replace(M=64, K=256, I=4608, E=8, topk=2, renormalize=False,
+                                                         logits_dist="normal"),
     # the same regime with I % 128 != 0: the general 128 x 128 tile kernel
     "bf16_tiled_I192": WORKLOADS["mixtral_bf16"].replace(M=700, K=384, I=192, E=4, topk=2, renormalize=False,
                                                          logits_dist="normal"),
