@@ -144,13 +144,14 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
   const int total = *g.t.tile_count * n_tiles;
   const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
   const int per = (total + 7) >> 3;
-  // An XCD's items past its last whole round (32 compute units) leave units
-  // idle; when they fill at most half a round after at least one whole round,
-  // each of them becomes two work items over the two halves of its rows,
-  // adjacent so that the pair shares its weight panel through L2.  The
-  // outputs are the same: every row is computed as in the whole item.
+  // An XCD's items past its last whole round (32 compute units), or all of
+  // them when there are fewer than a round, leave units idle; when they fill
+  // at most half a round, each of them becomes two work items over the two
+  // halves of its rows, adjacent so that the pair shares its weight panel
+  // through L2.  The outputs are the same: every row is computed as in the
+  // whole item (the fp8 epilogue's quantisation groups are per row).
   const int whole = per & ~(kXcdUnits - 1), rem = per - whole;
-  const bool split_tail = MOE_STREAM_SPLIT_TAIL && GATED && EB == 2 && whole > 0 && rem <= kXcdUnits / 2;
+  const bool split_tail = MOE_STREAM_SPLIT_TAIL && GATED && rem <= kXcdUnits / 2;
   int li = local, half = -1;
   if (split_tail && local >= whole) {
     li = whole + ((local - whole) >> 1);
@@ -546,8 +547,8 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
 template <int EB, bool GATED, int NBW, int D, int TMAX>
 hipError_t launch_cfg(int out_dtype, const GemmParams &g, int n_tiles, hipStream_t s) {
   const int64_t items = (int64_t)g.t.max_tiles * n_tiles;
-  // bf16 gated: room for a split tail (at most half a round more per XCD)
-  const int64_t extra = MOE_STREAM_SPLIT_TAIL && GATED && EB == 2 ? 8 * (kXcdUnits / 2) : 0;
+  // gated: room for a split tail (at most half a round more per XCD)
+  const int64_t extra = MOE_STREAM_SPLIT_TAIL && GATED ? 8 * (kXcdUnits / 2) : 0;
   dim3 grid((unsigned)(((items + 7) / 8) * 8 + extra)), block(kThreads);
   const bool bf = out_dtype == MOE_DTYPE_BF16;
   if (g.w_packed) {
