@@ -622,6 +622,11 @@ SHARD_CASES = {
     "bf16_batched": WORKLOADS["mixtral_bf16"].replace(M=150, K=256, I=128, E=12, topk=2, format=FORMAT_BATCHED,
                                                       capacity=150, logits_dist="normal"),
     "fp8_batched": WORKLOADS["decode_fp8_m64"].replace(M=80, K=256, I=256, E=12, topk=4, capacity=80),
+    # few experts and wide K (8 local of 24): the unsharded layer and every
+    # shard split the down GEMM over K, and a shard's permutation holds only
+    # its own picks
+    "bf16_split_k": WORKLOADS["mixtral_bf16"].replace(M=96, K=4096, I=512, E=24, topk=2, renormalize=True,
+                                                      logits_dist="normal"),
 }
 
 
@@ -655,6 +660,8 @@ def test_expert_parallel_shards(name):
         out, _, ws, p = U.run_forward(wls, U.to_cuda(ds))
         torch.cuda.synchronize()
         L = moe.workspace_layout(p)
+        if name == "bf16_split_k":
+            assert L.down_split == 2
         ids = U.ws_view(ws, L.topk_ids, wl.M * wl.topk).cpu().numpy()
         fids = U.ws_view(fws, moe.workspace_layout(U.problem(wl)).topk_ids, wl.M * wl.topk).cpu().numpy()
         np.testing.assert_array_equal(ids, fids)
