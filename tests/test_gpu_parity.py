@@ -529,6 +529,38 @@ def test_graph_replay_matches_eager():
         assert torch.equal(sout, e_sout), it
 
 
+def test_graph_replay_split_paths():
+    """The same for a layer whose gated GEMM runs its items as row halves (fewer
+    than half a round of items) and whose down GEMM splits K into fp32 partial
+    sums and a reduce: every replay bitwise equal to an eager run."""
+    wl = SMALL["bf16_split_k"]
+    d = U.to_cuda(make_inputs(wl, seed=24, device="cpu"))
+    p = U.problem(wl)
+    assert moe.workspace_layout(p).down_split == 2
+    ws = moe.empty_workspace(p)
+    out = torch.empty(wl.M, wl.K, dtype=torch.bfloat16, device="cuda")
+    U.run_forward(wl, d, ws=ws, p=p, out=out)   # warm-up
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            moe.moe_forward(p, d["logits"], d["x"], d["w1"], None, d["w2"], None, out, ws)
+    torch.cuda.synchronize()
+    ews = moe.empty_workspace(p)
+    for it in range(3):
+        fresh = make_inputs(wl, seed=200 + it, device="cpu")
+        d["logits"].copy_(fresh["logits"].cuda())
+        d["x"].copy_(fresh["x"].cuda())
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        e_out, _, _, _ = U.run_forward(wl, d, ws=ews, p=p)
+        torch.cuda.synchronize()
+        assert torch.equal(out, e_out), it
+
+
 # ---------------------------------------------------------------- packed weights
 
 PACK_CASES = {
