@@ -217,6 +217,10 @@ def main():
     # Timed region: K steps, each with stage events on the launch stream.
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(moe.NUM_STAGE_EVENTS)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # torch creates its HIP events at their first record: do that here, so that
+    # the timed steps do not create (and record twice) the stage events
+    for e in [start, end] + [e for row in evs for e in row]:
+        e.record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
