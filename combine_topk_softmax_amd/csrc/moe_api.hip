@@ -405,7 +405,7 @@ const char *moe_status_str(moe_status s) {
   return "unknown status";
 }
 
-int moe_version(void) { return 2; }
+int moe_version(void) { return 3; }
 
 moe_status moe_validate(const moe_problem *p) { return validate(p); }
 

@@ -197,6 +197,9 @@ typedef struct moe_ws_layout {
 } moe_ws_layout;
 
 const char *moe_status_str(moe_status s);
+/* ABI version, raised whenever a struct or a call changes: 3 (moe_ws_layout
+ * gained down_partial and down_split; a caller built against 2 passes a
+ * smaller moe_ws_layout to moe_workspace_layout). */
 int moe_version(void);
 
 /* Host-side check of a problem description (the asserts of

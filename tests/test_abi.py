@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = moe.load_library()
-    assert L.moe_version() == 2
+    assert L.moe_version() == 3
     assert moe.status_str(moe.MOE_OK) == "ok"
     assert "workspace" in moe.status_str(moe.MOE_ERR_WORKSPACE)
 
