@@ -74,6 +74,7 @@ EXPORTS = ("moe_status_str", "moe_version", "moe_validate", "moe_workspace_size"
            "moe_pack_weights", "moe_route", "moe_prepare", "moe_experts", "moe_finalize", "moe_shared_expert", "moe_forward")
 
 _lib = None
+ABI_VERSION = 3   # the struct layouts mirrored here
 
 
 def load_library(path: str = LIB_PATH):
@@ -87,6 +88,8 @@ def load_library(path: str = LIB_PATH):
     L.moe_status_str.restype = C.c_char_p
     L.moe_status_str.argtypes = [C.c_int]
     L.moe_version.restype = C.c_int
+    if L.moe_version() != ABI_VERSION:
+        raise ImportError(f"{path} has ABI version {L.moe_version()}, this binding expects {ABI_VERSION}: rebuild it")
     for name, args in {
         "moe_validate": [P(Problem)],
         "moe_workspace_size": [P(Problem), P(C.c_size_t)],
