@@ -97,7 +97,88 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ y, c
   }
 }
 
+// moe_forward with the down GEMM split over K (bf16): a pick's row is the sum
+// of its slot's fp32 partial slices in split order, rounded to bf16, which is
+// what the split's reduce would have stored; weighting and summing then go as
+// in combine_kernel, so the output equals reduce-then-combine bit for bit
+// without the reduce's launch and its bf16 round trip.  Groups of 4 picks keep
+// 2 x S 16-byte loads per pick in flight; the partial rows are read once.
+constexpr int kSplitGroup = 4;
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void combine_split_kernel(const float *__restrict__ part, int S, int64_t stride,
+                                                            const float *__restrict__ w,
+                                                            const int32_t *__restrict__ inv, int K, int k,
+                                                            uint16_t *__restrict__ out) {
+  const int m = blockIdx.x;
+  for (int c = threadIdx.x * 8; c < K; c += 256 * 8) {
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j0 = 0; j0 < k; j0 += kSplitGroup) {
+      int64_t slot[kSplitGroup];
+      float wj[kSplitGroup];
+#pragma unroll
+      for (int u = 0; u < kSplitGroup; ++u) {
+        slot[u] = -1;
+        wj[u] = 0.0f;
+        if (j0 + u < k) {
+          const int64_t pair = (int64_t)m * k + j0 + u;
+          const int64_t sl = inv[pair];
+          if (sl >= 0) {                           // else dropped, or another shard's pick
+            slot[u] = sl;
+            wj[u] = w ? w[pair] : 1.0f;
+          }
+        }
+      }
+      float v[kSplitGroup][8];
+#pragma unroll
+      for (int u = 0; u < kSplitGroup; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[u][i] = 0.0f;
+      for (int sk = 0; sk < S; ++sk) {
+        f32x4v lo[kSplitGroup], hi[kSplitGroup];
+#pragma unroll
+        for (int u = 0; u < kSplitGroup; ++u) {
+          if (slot[u] >= 0) {
+            const f32x4v *src = reinterpret_cast<const f32x4v *>(part + sk * stride + slot[u] * K + c);
+            lo[u] = __builtin_nontemporal_load(src);
+            hi[u] = __builtin_nontemporal_load(src + 1);
+          } else {
+            lo[u] = hi[u] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kSplitGroup; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[u][i] += lo[u][i];
+            v[u][4 + i] += hi[u][i];
+          }
+      }
+#pragma unroll
+      for (int u = 0; u < kSplitGroup; ++u) {
+        if (slot[u] < 0) continue;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += wj[u] * bf16_bits_to_f32(f32_to_bf16_bits(v[u][i]));
+      }
+    }
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = (uint32_t)f32_to_bf16_bits(acc[2 * i]) | ((uint32_t)f32_to_bf16_bits(acc[2 * i + 1]) << 16);
+    *reinterpret_cast<uint4 *>(out + (int64_t)m * K + c) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_combine_split(const moe_problem &p, const float *part, int S, int64_t stride,
+                                const float *topk_w, const int32_t *inv, void *out, hipStream_t s) {
+  if (p.act_dtype != MOE_DTYPE_BF16 || !inv) return hipErrorInvalidValue;
+  dim3 grid((unsigned)p.M), block(256);
+  combine_split_kernel<<<grid, block, 0, s>>>(part, S, stride, topk_w, inv, (int)p.K, (int)p.topk,
+                                              (uint16_t *)out);
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(const moe_problem &p, const void *fused_out, const float *topk_w,
                           const int32_t *inv, bool rows_from_inv, void *out, hipStream_t s) {

@@ -234,6 +234,13 @@ moe_status start_shared(const SharedStart &sh, hipStream_t main) {
   return MOE_OK;
 }
 
+// The down GEMM's K-split partial sums, when the caller combines them itself.
+struct SplitPartials {
+  const float *part = nullptr;   // null: the rows were reduced into fused_out
+  int S = 0;
+  int64_t stride = 0;
+};
+
 // sh: start the shared expert once the gated grouped GEMM is queued.  Its
 // GEMMs fill every compute unit: started with the layer, they held the units
 // the short counting and planning kernels waited for (DeepSeek-V3 shape:
@@ -241,7 +248,8 @@ moe_status start_shared(const SharedStart &sh, hipStream_t main) {
 // 0.35 ms; overlapping the down GEMM costs about 0.3 ms and measured best.
 moe_status do_experts(const moe_problem &p, const void *a, const float *a_scale, const moe_weights &w,
                       const int32_t *counts, void *fused_out, void *ws, const moe_ws_layout &L,
-                      hipStream_t s, const moe_stage_events *ev, const SharedStart *sh = nullptr) {
+                      hipStream_t s, const moe_stage_events *ev, const SharedStart *sh = nullptr,
+                      SplitPartials *sp = nullptr) {
   const bool standard = p.format == MOE_FORMAT_STANDARD;
   const bool fp8 = fp8_path(p);
   const int64_t I = p.N / 2;
@@ -333,8 +341,15 @@ moe_status do_experts(const moe_problem &p, const void *a, const float *a_scale,
     g2.k_split = (int)split;
     g2.split_stride = L.perm_len * p.K;
     MOE_HIP(launch_stream_gemm(p.w_dtype, MOE_DTYPE_F32, kGemmDown, g2, (int)(p.K / 128), 2, s));
-    MOE_HIP(launch_split_reduce(at<float>(ws, L.down_partial), (int)split, g2.split_stride, perm, L.perm_len,
-                                g2.n_pairs, (int)p.K, p.act_dtype, fused_out, s));
+    if (sp) {
+      // sp: the caller's combine reads the partial sums (fused_out stays unwritten)
+      sp->part = at<float>(ws, L.down_partial);
+      sp->S = (int)split;
+      sp->stride = g2.split_stride;
+    } else {
+      MOE_HIP(launch_split_reduce(at<float>(ws, L.down_partial), (int)split, g2.split_stride, perm, L.perm_len,
+                                  g2.n_pairs, (int)p.K, p.act_dtype, fused_out, s));
+    }
   } else if (streaming)
     MOE_HIP(launch_stream_gemm(p.w_dtype, p.act_dtype, kGemmDown, g2, (int)(p.K / 128),
                                stream_gemm_down_blocks(p.w_dtype, p.E, local_pairs, p.K, I), s));
@@ -547,10 +562,11 @@ moe_status moe_forward(const moe_problem *p, const float *logits, const void *x,
   float *a_s = quant ? at<float>(workspace, L.a_scale) : nullptr;
   int32_t *counts = at<int32_t>(workspace, L.counts);
   void *fused = at<void>(workspace, L.fused_out);
+  SplitPartials sp;   // set when the down GEMM split K: the combine reads its partial sums
   if (!chunked(*p)) {
     if ((st = do_prepare(*p, x, ti, tw, a_q, a_s, counts, workspace, L, stream)) != MOE_OK) return st;
     if ((st = do_experts(*p, a_q ? a_q : x, a_s, *w, counts, fused, workspace, L, stream, events,
-                         shared ? &sh : nullptr)) != MOE_OK)
+                         shared ? &sh : nullptr, &sp)) != MOE_OK)
       return st;
   } else {
     // Prepare the whole batch's rows, then count, permute and run the experts
@@ -571,8 +587,11 @@ moe_status moe_forward(const moe_problem *p, const float *logits, const void *x,
     }
   }
   // the permutation prepare just wrote masks dropped / other shards' pairs
-  MOE_HIP(launch_combine(*p, fused, p->apply_router_weight_on_input ? nullptr : tw,
-                         at<int32_t>(workspace, L.inv), !standard, out, stream));
+  const float *cw = p->apply_router_weight_on_input ? nullptr : tw;
+  if (sp.part)
+    MOE_HIP(launch_combine_split(*p, sp.part, sp.S, sp.stride, cw, at<int32_t>(workspace, L.inv), out, stream));
+  else
+    MOE_HIP(launch_combine(*p, fused, cw, at<int32_t>(workspace, L.inv), !standard, out, stream));
   record(events, 5, stream);
   if (shared) MOE_HIP(hipStreamWaitEvent(stream, shared->output_ready, 0));
   return MOE_OK;

@@ -253,6 +253,10 @@ hipError_t launch_pack_weights(const void *src, void *dst, int64_t E, int64_t Nw
 // outputs are added unweighted (router weight applied on the input).
 hipError_t launch_combine(const moe_problem &p, const void *fused_out, const float *topk_w,
                           const int32_t *inv, bool rows_from_inv, void *out, hipStream_t s);
+// The combine of moe_forward when the down GEMM split K (bf16, Standard): the
+// pair rows come from the split's fp32 partial slices by slot (inv[pair]).
+hipError_t launch_combine_split(const moe_problem &p, const float *part, int S, int64_t stride,
+                                const float *topk_w, const int32_t *inv, void *out, hipStream_t s);
 
 constexpr int kTileRows = 128;   // grouped-GEMM rows per tile (BM)
 constexpr int kMinPlanTileRows = 96;   // the smallest row tile any GEMM's plan uses (wide fp8 panels)

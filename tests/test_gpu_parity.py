@@ -467,8 +467,10 @@ def test_forward_is_deterministic():
 
 def test_stage_calls_equal_forward():
     """route -> prepare -> experts -> finalize through the separate calls
-    gives exactly what moe_forward gives (same kernels, same order)."""
-    for wl in (SMALL["bf16_ragged"], SMALL["fp8_batched"]):
+    gives exactly what moe_forward gives (same kernels, same order; with the
+    down GEMM split over K, moe_experts reduces the partial sums into the pair
+    rows and moe_forward's combine reads them directly, bit for bit the same)."""
+    for wl in (SMALL["bf16_ragged"], SMALL["fp8_batched"], SMALL["bf16_split_k"], SMALL["bf16_split_k_zipf"]):
         d = U.to_cuda(make_inputs(wl, seed=22, device="cpu"))
         ref, _, _, p = U.run_forward(wl, d)
         ws = moe.empty_workspace(p)
