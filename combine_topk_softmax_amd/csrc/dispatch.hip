@@ -21,6 +21,7 @@ namespace moe {
 namespace {
 
 constexpr int kMaxExperts = 1024;
+constexpr int kMaxChunks = 64;   // counting chunks per batch (the workspace layout keeps to it)
 
 // ----------------------------------------------------------- histogram
 
@@ -84,12 +85,18 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t *__restrict__ chunk_
   if (e == 0 && clear_status) *status = 0;
   int run = 0;
   if (e < E) {
-    for (int c = 0; c < n_chunks; ++c) {
-      int64_t i = (int64_t)c * E + e;
-      int h = chunk_hist[i];
-      chunk_hist[i] = run;
-      run += h;
-    }
+    // the expert's column of chunk counts into registers first, so that the
+    // loads are in flight together rather than each behind the last store
+    int h[kMaxChunks];
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c)
+      if (c < n_chunks) h[c] = chunk_hist[(int64_t)c * E + e];
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c)
+      if (c < n_chunks) {
+        chunk_hist[(int64_t)c * E + e] = run;
+        run += h[c];
+      }
     counts[e] = run;
     expert_num_tokens[e] = run;
   }
@@ -340,6 +347,7 @@ hipError_t launch_count_and_permute(const moe_problem &p, const int32_t *ids,
                                                           b.chunk_hist);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (b.n_chunks > kMaxChunks) return hipErrorInvalidValue;
   scan_kernel<<<1, 1024, 0, s>>>(b.chunk_hist, (int)b.n_chunks, E, align, standard, b.counts,
                                  expert_num_tokens, b.offsets, b.perm, b.perm_len, b.status, b.clear_status);
   err = hipGetLastError();
