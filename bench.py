@@ -7,8 +7,11 @@ over one batch of synthetic tokens already resident in HBM, through the C ABI
 of the dominant kernel (the gated grouped GEMM, timed with HIP events on the
 stream it runs on) and the CPU oracle's throughput on a bounded sample.
 
-Default workload: Mixtral-style bf16 prefill, M=512 tokens, hidden 4096,
-expert intermediate 14336, 8 experts, top-2 softmax renormalised.
+Default workload: the skewed bf16 prefill, M=16384 tokens, hidden 4096,
+expert intermediate 1536, 128 experts, top-8 softmax over Zipf(1.2)-biased
+logits -- the largest of the workloads, and the one whose grouped GEMMs are
+bound by the matrix cores.  `--workload` selects the others.  Each run also
+times hipGraph replay of the same step (`graph_ms_per_step`).
 """
 from __future__ import annotations
 
@@ -35,11 +38,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mixtral_bf16")
+    ap.add_argument("--workload", default="skewed_bf16")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens of the CPU-oracle sample (0: sized to ~15 s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--graph", action="store_true", help="also time hipGraph replay of the step")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="skip timing hipGraph replay of the step (timed by default)")
     ap.add_argument("--weights", choices=["packed", "row_major"], default="packed",
                     help="expert weight layout (packed once before timing, as at model load)")
     ap.add_argument("--chunk-tokens", type=int, default=0,
@@ -98,6 +102,17 @@ def measured_traffic(workload: str):
     return t.get("hbm_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, d, sample_tokens: int):
     import oracle
     from workloads import sample_tokens as pick
@@ -114,7 +129,7 @@ def cpu_baseline(wl, d, sample_tokens: int):
     t0 = time.perf_counter()
     oracle.moe_tokens(wl, host, toks)
     dt = time.perf_counter() - t0
-    return {"value": len(toks) / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": len(toks) / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle", "cpu": cpu_model(),
             "sample": f"{len(toks)} of {wl.M} tokens of {wl.name} (router over all {wl.M} tokens, "
                       f"then the expert MLPs and combine of the sampled tokens), float64 C, {dt:.1f} s"}
 

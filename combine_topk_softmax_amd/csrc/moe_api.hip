@@ -509,9 +509,11 @@ moe_status moe_finalize(const moe_problem *p, const void *fused_out, const float
   if ((st = check_ws(*p, workspace, workspace_bytes, L)) != MOE_OK) return st;
   if (!fused_out || !out || (!topk_weights && !p->apply_router_weight_on_input)) return MOE_ERR_INVALID_ARG;
   const bool batched = p->format == MOE_FORMAT_BATCHED_EXPERTS;
-  const int32_t *inv = batched || p->expert_map ? at<int32_t>(workspace, L.inv) : nullptr;
-  MOE_HIP(launch_combine(*p, fused_out, p->apply_router_weight_on_input ? nullptr : topk_weights, inv, batched,
-                         out, stream));
+  // the pair -> slot map moe_prepare wrote masks every pair it did not place
+  // (bad ids, other shards' picks, dropped batched picks), whose rows of
+  // fused_out the experts step never wrote
+  MOE_HIP(launch_combine(*p, fused_out, p->apply_router_weight_on_input ? nullptr : topk_weights,
+                         at<int32_t>(workspace, L.inv), batched, out, stream));
   return MOE_OK;
 }
 

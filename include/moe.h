@@ -271,10 +271,11 @@ moe_status moe_experts(const moe_problem *p, const void *a, const float *a_scale
 /* [Combine] (FusedMoEPrepareAndFinalize.finalize with a TopKWeightAndReduce):
  * out[m, :] = sum_j topk_weights[m, j] * fused_out[pair (m, j), :], summed in
  * fp32 in j order, written in act_dtype; out [M, K] is fully overwritten.
- * BATCHED_EXPERTS, and STANDARD with an expert_map, read the pair -> row map
- * moe_prepare left in the workspace; dropped pairs and other shards' picks
- * contribute nothing.  With apply_router_weight_on_input the weights are not
- * applied again (topk_weights may be NULL). */
+ * It reads the pair -> row map moe_prepare left in the same workspace (so
+ * moe_prepare of this step must have run on it): pairs with a bad expert id,
+ * dropped batched pairs and other shards' picks contribute nothing, and their
+ * fused_out rows are never read.  With apply_router_weight_on_input the
+ * weights are not applied again (topk_weights may be NULL). */
 moe_status moe_finalize(const moe_problem *p, const void *fused_out, const float *topk_weights,
                         void *out, void *workspace, size_t workspace_bytes, hipStream_t stream);
 

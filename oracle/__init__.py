@@ -104,6 +104,12 @@ def _np(t, dtype=None) -> Optional[np.ndarray]:
 
 # ------------------------------------------------------------------- API
 
+def host_array(t) -> Optional[np.ndarray]:
+    """A host copy of a tensor in the form the calls below take (bf16 as uint16
+    bits, fp8 as uint8 codes), to hand the same large tensor to many calls."""
+    return _np(t)
+
+
 def e4m3_decode(codes) -> np.ndarray:
     c = np.ascontiguousarray(codes, dtype=np.uint8)
     out = np.empty(c.shape, np.float64)

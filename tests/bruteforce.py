@@ -41,15 +41,30 @@ def gated(G, U, gelu=False):
     return G * (sps.ndtr(G) if gelu else sps.expit(G)) * U
 
 
+def capacity_keep(ids: np.ndarray, capacity: int) -> np.ndarray:
+    """Batched (worst-tokens) layout with `capacity` rows per expert: a pick is
+    kept when fewer than `capacity` earlier picks (in token order) went to the
+    same expert.  Ranks come from numpy's stable argsort of the flat ids, so
+    ties in expert keep their token order."""
+    flat = np.asarray(ids).ravel()
+    order = np.argsort(flat, kind="stable")
+    rank = np.empty(flat.size, np.int64)
+    sorted_ids = flat[order]
+    starts = np.searchsorted(sorted_ids, sorted_ids, side="left")
+    rank[order] = np.arange(flat.size) - starts
+    return (rank < capacity).reshape(np.asarray(ids).shape)
+
+
 def dense_moe(logits, x, w1, w2, k, sigmoid=False, renorm=False, fp8_act=False, gelu=False,
-              expert_map=None, weight_on_input=False, bf16_input=False):
+              expert_map=None, weight_on_input=False, bf16_input=False, capacity=None):
     """out[m] = sum_j w[m,j] * expert_{id[m,j]}(x[m]) with every expert evaluated densely.
 
     x [M, K], w1 [E, 2I, K], w2 [E, K, I] as float64 arrays (already dequantised).
     expert_map [global E]: local expert of each global one, -1 for another shard's
     (those picks add nothing).  weight_on_input (k = 1): the input row is w * x,
     rounded to fp32 (numpy's float32 product) and to bf16 (torch's cast) when
-    bf16_input, and the expert output is added unweighted."""
+    bf16_input, and the expert output is added unweighted.  capacity: the
+    batched layout's rows per expert; picks past it (capacity_keep) add nothing."""
     x = np.asarray(x, np.float64)
     w1 = np.asarray(w1, np.float64)
     w2 = np.asarray(w2, np.float64)
@@ -71,11 +86,12 @@ def dense_moe(logits, x, w1, w2, k, sigmoid=False, renorm=False, fp8_act=False, 
     if fp8_act:
         A = np.stack([fp8_group_quant_torch(A[e].astype(np.float32)) for e in range(E)])
     Y = np.einsum("emi,eki->emk", A, w2)               # [E, M, K]
+    keep = np.ones(ids.shape, bool) if capacity is None else capacity_keep(ids, capacity)
     out = np.zeros((M, K))
     for m in range(M):
         for j in range(k):
             e = ids[m, j] if expert_map is None else expert_map[ids[m, j]]
-            if e < 0:
+            if e < 0 or not keep[m, j]:
                 continue
             out[m] += (1.0 if weight_on_input else wts[m, j]) * Y[e, m]
     return out, ids, wts

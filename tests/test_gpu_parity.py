@@ -171,6 +171,14 @@ SMALL = {
     "bf16_mfma_batched": WORKLOADS["mixtral_bf16"].replace(M=600, K=256, I=128, E=3, topk=2,
                                                            format=FORMAT_BATCHED, capacity=600,
                                                            logits_dist="normal"),
+    # 256 x 256 MFMA tiles past one L2 group of row tiles: 12 row tiles (a
+    # whole group of 8 and a partial one of 4) x 2 column tiles, and 18 row
+    # tiles (two whole groups and a partial one of 2) with Zipf routing
+    "bf16_mfma_groups": WORKLOADS["mixtral_bf16"].replace(M=1200, K=512, I=256, E=4, topk=2, renormalize=False,
+                                                          logits_dist="normal"),
+    "bf16_mfma_18tiles": WORKLOADS["mixtral_bf16"].replace(M=2000, K=256, I=256, E=3, topk=2, renormalize=False,
+                                                           logits_dist="normal"),
+    "bf16_mfma_zipf": WORKLOADS["skewed_bf16"].replace(M=1500, K=256, I=256, E=16, topk=4),
     # weight streaming with enough (expert, column tile) items that the down
     # GEMM gives each wavefront two 16-row weight blocks
     "bf16_down2": WORKLOADS["mixtral_bf16"].replace(M=256, K=2048, I=128, E=64, topk=4, renormalize=False,
@@ -232,6 +240,15 @@ def test_experts_parity_every_pair(name):
     fused = torch.full((rows, wl.K), float("nan"), dtype=U.torch_act_dtype(wl), device="cuda")
     moe.moe_experts(p, a_out if a_out is not None else g["x"], a_scale, g["w1"], g.get("w1_scale"), g["w2"],
                     g.get("w2_scale"), counts, fused, ws)
+    if wl.I % 128 == 0:
+        # the packed weight layout reorders bytes only: bitwise the same rows
+        pp = U.problem(wl, weight_layout=moe.WEIGHTS_PACKED)
+        w1p, w2p = moe.pack_weights(pp, g["w1"], g["w2"])
+        fused_p = torch.full_like(fused, float("nan"))
+        moe.moe_experts(pp, a_out if a_out is not None else g["x"], a_scale, w1p, g.get("w1_scale"), w2p,
+                        g.get("w2_scale"), counts, fused_p, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(fused_p.view(torch.int16), fused.view(torch.int16))
     torch.cuda.synchronize()
     got = fused.float().cpu().numpy()
     L = moe.workspace_layout(p)
@@ -318,16 +335,18 @@ def test_finalize_parity():
         ids, w = _ids_from_oracle(wl)
         rows = wl.E * wl.capacity if bat else wl.M * wl.topk
         y = torch.randn(rows, wl.K, generator=gen).to(U.torch_act_dtype(wl))
-        if bat:   # the combine reads the pair -> row map that prepare leaves in the workspace
-            counts = torch.empty(wl.E, dtype=torch.int32, device="cuda")
+        # the combine reads the pair -> row map that prepare leaves in the workspace
+        counts = torch.empty(wl.E, dtype=torch.int32, device="cuda")
+        x = torch.zeros(wl.M, wl.K, dtype=U.torch_act_dtype(wl), device="cuda")
+        if bat:
             a_out = torch.empty(wl.E, wl.capacity, wl.K, dtype=torch.uint8, device="cuda")
             a_s = torch.empty(wl.E * wl.capacity, wl.K // 128, device="cuda")
-            x = torch.zeros(wl.M, wl.K, dtype=U.torch_act_dtype(wl), device="cuda")
             moe.moe_prepare(p, x, torch.from_numpy(ids).cuda(), a_out, a_s, counts, ws)
             _, inv = oracle.permute_batched(ids, wl.E, wl.capacity)
             ypairs = y.float().numpy()[np.maximum(inv, 0)]
             keep = (inv >= 0).astype(np.int32)
         else:
+            moe.moe_prepare(p, x, torch.from_numpy(ids).cuda(), None, None, counts, ws)
             ypairs, keep = y.float().numpy(), None
         out = torch.empty(wl.M, wl.K, dtype=U.torch_act_dtype(wl), device="cuda")
         wt = torch.from_numpy(w.astype(np.float32))
@@ -337,19 +356,98 @@ def test_finalize_parity():
         assert U.rel_err(out.float().cpu().numpy(), ref) <= U.tol_for(wl)
 
 
+def test_finalize_ignores_bad_id_pairs():
+    """A pick with an out-of-range expert id is flagged by prepare and adds
+    nothing in finalize: its row of the expert output (left NaN here, as the
+    experts step never writes it) is not read."""
+    wl = SMALL["bf16_ragged"]
+    d = U.to_cuda(make_inputs(wl, seed=24, device="cpu"))
+    p = U.problem(wl)
+    ws = moe.empty_workspace(p)
+    w = torch.empty(wl.M, wl.topk, device="cuda")
+    ids = torch.empty(wl.M, wl.topk, dtype=torch.int32, device="cuda")
+    moe.moe_route(p, d["logits"], w, ids)
+    bad = [(3, 1), (wl.M - 1, 0)]
+    ids[3, 1] = wl.E
+    ids[wl.M - 1, 0] = -7
+    counts = torch.empty(wl.E, dtype=torch.int32, device="cuda")
+    moe.moe_prepare(p, d["x"], ids, None, None, counts, ws)
+    fused = torch.full((wl.M * wl.topk, wl.K), float("nan"), dtype=torch.bfloat16, device="cuda")
+    moe.moe_experts(p, d["x"], None, d["w1"], None, d["w2"], None, counts, fused, ws)
+    out = torch.empty(wl.M, wl.K, dtype=torch.bfloat16, device="cuda")
+    moe.moe_finalize(p, fused, w, out, ws)
+    torch.cuda.synchronize()
+    L = moe.workspace_layout(p)
+    assert U.ws_view(ws, L.status, 1).item() & moe.DEVICE_BAD_EXPERT_ID
+    keep = np.ones((wl.M, wl.topk), np.int32)
+    for m, j in bad:
+        keep[m, j] = 0
+    y = fused.float().cpu().numpy().reshape(wl.M, wl.topk, wl.K)
+    assert np.isnan(y[keep == 0]).all() and np.isfinite(y[keep == 1]).all()
+    ref = oracle.combine(w.cpu().double().numpy(), np.where(keep[..., None] == 1, y, 0.0), keep)
+    got = out.float().cpu().numpy()
+    assert np.all(np.isfinite(got))
+    assert U.rel_err(got, ref) <= U.tol_for(wl)
+
+
 # ---------------------------------------------------------------- whole layer
 
 FULL = list(WORKLOADS)
+# token rows whose whole layer output the full-size test compares (all of
+# them where the oracle finishes in seconds); the larger workloads compare a
+# sample of tokens plus expert-output rows covering every 32-row block of every
+# expert segment (below)
+FULL_ALL_TOKENS = {"tiny_fp32", "mixtral_bf16", "decode_fp8_m64", "decode_fp8_m256"}
+
+
+def _segment_block_pairs(counts, offsets, perm, block=32, seed=0):
+    """One pair from every `block`-row block of every expert's segment of the
+    Standard permutation, plus each segment's last row: every row tile of any
+    grouped-GEMM tiling by multiples of `block` (and every column tile of it,
+    as each row is compared in full) holds a checked pair."""
+    rng = np.random.default_rng(seed)
+    picks = set()
+    for e in range(len(counts)):
+        c, base = int(counts[e]), int(offsets[e])
+        for b0 in range(0, c, block):
+            picks.add(base + b0 + int(rng.integers(min(block, c - b0))))
+        if c:
+            picks.add(base + c - 1)
+    return sorted(int(perm[s]) for s in picks)
+
+
+def _check_pair_rows(wl, d, ws, L, rids, pairs):
+    """Unweighted expert output rows (M, k, K) that moe_forward left in its
+    workspace, against the oracle's expert MLP of each pair."""
+    fused = U.ws_view(ws, L.fused_out, wl.M * wl.topk * wl.K, torch.bfloat16)
+    got = fused.view(wl.M * wl.topk, wl.K)[torch.tensor(pairs, device="cuda")].float().cpu().numpy()
+    x, w1, w2 = (oracle.host_array(d[k]) for k in ("x", "w1", "w2"))
+    ref = np.empty_like(got, dtype=np.float64)
+    last_m, a = -1, None
+    for i, f in enumerate(pairs):
+        m, j = divmod(f, wl.topk)
+        if m != last_m:
+            a, last_m = oracle.input_row(x, m, wl.act_dtype), m
+        _, ref[i] = oracle.expert_row(a, int(rids[m, j]), w1, w2, wl.w_dtype, wl.I)
+    assert np.all(np.isfinite(got))
+    return U.rel_err(got, ref)
 
 
 @pytest.mark.parametrize("name", FULL)
 def test_forward_parity_full_size(name):
+    """Every workload at full size, in the launch configuration the benchmark
+    times (packed expert weights where the shape allows)."""
     wl = WORKLOADS[name]
     small = wl.M * wl.K * wl.I * wl.E < 2 ** 28
     d = make_inputs(wl, seed=0, device="cpu" if small else "cuda")
     g = U.to_cuda(d)
-    out, sout, ws, p = U.run_forward(wl, g)
+    p = None
+    if wl.I % 128 == 0:
+        p = U.problem(wl, weight_layout=moe.WEIGHTS_PACKED)
+        g["w1"], g["w2"] = moe.pack_weights(p, g["w1"], g["w2"])
+    out, sout, ws, p = U.run_forward(wl, g, p=p)
     torch.cuda.synchronize()
+    del g
     L = moe.workspace_layout(p)
     # every routing / counting / permutation entry
     rids, rw = oracle.route(d["logits"], wl.topk, wl.scoring, wl.renormalize)
@@ -365,13 +463,19 @@ def test_forward_parity_full_size(name):
         np.testing.assert_array_equal(U.ws_view(ws, L.offsets, wl.E + 1).cpu().numpy(), roff)
     np.testing.assert_array_equal(U.ws_view(ws, L.counts, wl.E).cpu().numpy(), rc)
     assert U.ws_view(ws, L.status, 1).item() == 0
-    # output rows: all of them for small problems, a seeded sample otherwise
-    toks = list(range(wl.M)) if small else sample_tokens(wl.M, 10, seed=1)
+    if name not in FULL_ALL_TOKENS:
+        # expert-output rows from every 32-row block of every expert segment
+        assert not U.batched(wl) and L.down_split == 1
+        pairs = _segment_block_pairs(rc, roff, rperm, seed=9)
+        perr = _check_pair_rows(wl, d, ws, L, rids, pairs)
+        print(f"  {name}: {len(pairs)} expert-output rows, max rel err {perr:.3e}", flush=True)
+        assert perr <= U.tol_for(wl)
+    toks = list(range(wl.M)) if name in FULL_ALL_TOKENS else sample_tokens(wl.M, 10, seed=1)
     ref, _, _ = oracle.moe_tokens(wl, d, toks)
     got = out.float().cpu().numpy()[toks]
     assert np.all(np.isfinite(got))
     err = U.rel_err(got, ref)
-    print(f"  {name}: {len(toks)} rows, max rel err {err:.3e}", flush=True)
+    print(f"  {name}: {len(toks)} token rows, max rel err {err:.3e}", flush=True)
     assert err <= U.tol_for(wl)
     if wl.shared_I:
         sref = oracle.dense_mlp_tokens(d["x"], d["w1s"], d["w2s"], wl.shared_I, wl.act_dtype, toks)
@@ -596,7 +700,7 @@ def test_packed_weights_give_identical_results(name):
     assert torch.equal(got, ref)
 
 
-@pytest.mark.parametrize("name", ["mixtral_bf16", "dsv3_bf16", "decode_fp8_m64", "decode_fp8_m256"])
+@pytest.mark.parametrize("name", ["mixtral_bf16", "dsv3_bf16", "decode_fp8_m64", "decode_fp8_m256", "skewed_bf16"])
 def test_packed_weights_full_size(name):
     """The configuration the benchmark times (packed weights, full size):
     bitwise equal to the row-major run and within the bar of the oracle."""

@@ -243,6 +243,46 @@ def test_fp8_layer_matches_dense_brute_force():
     assert rel <= 1e-3
 
 
+@pytest.mark.parametrize("cap", [1, 3, 7])
+def test_batched_capacity_drop_matches_brute_force(cap):
+    """Worst-tokens layout with fewer rows per expert than some experts
+    receive: the picks whose rank in their expert (token order) reaches the
+    capacity are dropped and add nothing to their token's output."""
+    M, K, I, E, k = 24, 8, 4, 4, 2
+    d = _tiny(M, K, I, E, k, seed=77 + cap)
+    wl = _wl(M, K, I, E, k, format=oracle.BATCHED, capacity=cap)
+    out, ids, _ = oracle.moe_tokens(wl, d)
+    keep = bf.capacity_keep(ids, cap)
+    # the rank rule itself, counted pick by pick in token order
+    seen = {}
+    for m in range(M):
+        for j in range(k):
+            e = int(ids[m, j])
+            assert keep[m, j] == (seen.get(e, 0) < cap)
+            seen[e] = seen.get(e, 0) + 1
+    assert keep.any() and not keep.all()
+    ref, _, _ = bf.dense_moe(d["logits"], d["x"], d["w1"], d["w2"], k, capacity=cap)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-14)
+    undropped, _, _ = bf.dense_moe(d["logits"], d["x"], d["w1"], d["w2"], k)
+    assert np.abs(out - undropped).max() > 1e-3 * np.abs(undropped).max()
+
+
+def test_fp8_capacity_drop_matches_dense_brute_force():
+    # the tiny fp8 batched layer with 2 rows per expert buffer: most picks dropped
+    wl = WORKLOADS["decode_fp8_m64"].replace(M=6, K=256, I=128, E=4, topk=2, capacity=2)
+    d = make_inputs(wl, seed=3, device="cpu")
+    out, ids, _ = oracle.moe_tokens(wl, d)
+    assert not bf.capacity_keep(ids, 2).all()
+    w1 = (d["w1"].view(torch.float8_e4m3fn).to(torch.float64)
+          * torch.repeat_interleave(torch.repeat_interleave(d["w1_scale"].double(), 128, 1), 128, 2)).numpy()
+    w2 = (d["w2"].view(torch.float8_e4m3fn).to(torch.float64)
+          * torch.repeat_interleave(torch.repeat_interleave(d["w2_scale"].double(), 128, 1), 128, 2)).numpy()
+    ref, _, _ = bf.dense_moe(d["logits"].numpy(), d["x"].float().numpy(), w1, w2, wl.topk, fp8_act=True,
+                             capacity=2)
+    rel = np.abs(out - ref).max() / np.abs(ref).max()
+    assert rel <= 1e-3
+
+
 def test_golden_expert_closed_form():
     g = _load("expert_closed_form.json")
     x = np.array(g["x"], np.float32)
@@ -522,6 +562,9 @@ MUTANTS = [
     ("batched capacity check off by one", "inv[f] = r < cap ? (int32_t)(e * cap + r) : -1;",
      "inv[f] = r <= cap ? (int32_t)(e * cap + r) : -1;",
      [lambda: test_batched_slots(5)]),
+    ("batched capacity drop ignored", "keep[j] = lids[m * k + j] >= 0 && !(inv && inv[m * k + j] < 0);",
+     "keep[j] = lids[m * k + j] >= 0;",
+     [lambda: test_batched_capacity_drop_matches_brute_force(3), test_fp8_capacity_drop_matches_dense_brute_force]),
     ("group maximum taken over signed values", "float a = fabsf(xg[i]);", "float a = xg[i];",
      [test_quant_g128_matches_torch_and_bounds]),
 ]
