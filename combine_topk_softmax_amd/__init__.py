@@ -71,10 +71,12 @@ class WsLayout(C.Structure):
 
 
 EXPORTS = ("moe_status_str", "moe_version", "moe_validate", "moe_workspace_size", "moe_workspace_layout",
-           "moe_pack_weights", "moe_route", "moe_prepare", "moe_experts", "moe_finalize", "moe_shared_expert", "moe_forward")
+           "moe_pack_weights", "moe_route", "moe_prepare", "moe_experts", "moe_finalize", "moe_shared_expert", "moe_forward",
+           "moe_forward_noalloc")
 
 _lib = None
-ABI_VERSION = 3   # the struct layouts mirrored here
+ABI_VERSION = 4   # the struct layouts and calls mirrored here
+STATIC_SCRATCH_BYTES = 64 << 20   # MOE_STATIC_SCRATCH_BYTES of moe_forward_noalloc
 
 
 def load_library(path: str = LIB_PATH):
@@ -101,6 +103,7 @@ def load_library(path: str = LIB_PATH):
         "moe_finalize": [P(Problem), vp, vp, vp, vp, C.c_size_t, vp],
         "moe_shared_expert": [P(Problem), vp, vp, vp, vp, vp, C.c_size_t, vp],
         "moe_forward": [P(Problem), vp, vp, P(Weights), vp, P(Shared), vp, C.c_size_t, vp, P(StageEvents)],
+        "moe_forward_noalloc": [P(Problem), vp, vp, P(Weights), vp, P(Shared), vp, P(StageEvents), vp],
     }.items():
         f = getattr(L, name)
         f.restype = C.c_int
@@ -240,12 +243,7 @@ class SharedExpertStreams:
         self.output_ready = torch.cuda.Event()
 
 
-def moe_forward(p: Problem, logits, x, w1, w1_scale, w2, w2_scale, out, workspace, stream=None,
-                shared=None, shared_streams: Optional[SharedExpertStreams] = None, events=None):
-    """shared = (w1s, w2s, shared_out); events = list of torch.cuda.Event (timing) or None."""
-    L = load_library()
-    wp, wn = _ws(workspace)
-    w = _weights(w1, w1_scale, w2, w2_scale)
+def _shared_and_events(shared, shared_streams, events):
     sh = None
     if shared is not None:
         if shared_streams is None:
@@ -258,6 +256,27 @@ def moe_forward(p: Problem, logits, x, w1, w1_scale, w2, w2_scale, out, workspac
         ev = StageEvents()
         for i, e in enumerate(events[:NUM_STAGE_EVENTS]):
             ev.ev[i] = _event_handle(e) if e is not None else None
-    _check(L.moe_forward(C.byref(p), _ptr(logits), _ptr(x), C.byref(w), _ptr(out),
-                         C.byref(sh) if sh is not None else None, wp, wn, _stream(stream),
-                         C.byref(ev) if ev is not None else None), "moe_forward")
+    return (C.byref(sh) if sh is not None else None), (C.byref(ev) if ev is not None else None)
+
+
+def moe_forward(p: Problem, logits, x, w1, w1_scale, w2, w2_scale, out, workspace, stream=None,
+                shared=None, shared_streams: Optional[SharedExpertStreams] = None, events=None):
+    """shared = (w1s, w2s, shared_out); events = list of torch.cuda.Event (timing) or None."""
+    L = load_library()
+    wp, wn = _ws(workspace)
+    w = _weights(w1, w1_scale, w2, w2_scale)
+    sh, ev = _shared_and_events(shared, shared_streams, events)
+    _check(L.moe_forward(C.byref(p), _ptr(logits), _ptr(x), C.byref(w), _ptr(out), sh, wp, wn, _stream(stream),
+                         ev), "moe_forward")
+
+
+def moe_forward_noalloc(p: Problem, logits, x, w1, w1_scale, w2, w2_scale, out, stream=None, shared=None,
+                        shared_streams: Optional[SharedExpertStreams] = None, events=None, status_out=None):
+    """moe_forward on the library's own static workspace (no caller workspace,
+    no allocation); status_out: optional device int32 tensor of one element
+    that receives the call's device status word."""
+    L = load_library()
+    w = _weights(w1, w1_scale, w2, w2_scale)
+    sh, ev = _shared_and_events(shared, shared_streams, events)
+    _check(L.moe_forward_noalloc(C.byref(p), _ptr(logits), _ptr(x), C.byref(w), _ptr(out), sh, _stream(stream),
+                                 ev, _ptr(status_out)), "moe_forward_noalloc")

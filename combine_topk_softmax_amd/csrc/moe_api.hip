@@ -5,10 +5,19 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "moe_device.h"
 
 using namespace moe;
+
+// Library-held workspace of moe_forward_noalloc, used instead of a caller
+// buffer.  Each GPU the library runs on holds its own copy until the process
+// ends.  In host code `scratch` is only a host-side stand-in for the symbol:
+// its device address on the current GPU comes from hipGetSymbolAddress (once
+// per device, static_scratch below) and only that address is handed to
+// kernels.
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -405,6 +414,47 @@ moe_status do_shared(const moe_problem &p, const void *x, const void *w1, const 
   return MOE_OK;
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the device of `stream`, which must be
+// the current device (the lookup is made with that device current).
+moe_status static_scratch(hipStream_t stream, void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MOE_ERR_HIP;
+  if (dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return MOE_ERR_HIP;
+    if (sdev != dev) return MOE_ERR_INVALID_ARG;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+// The argument checks of moe_forward (M > 0).
+moe_status forward_args(const moe_problem &p, const float *logits, const void *x, const moe_weights *w,
+                        const void *out, const moe_shared *shared) {
+  if (!logits || !x || !w || !w->w1 || !w->w2 || !out) return MOE_ERR_INVALID_ARG;
+  if (fp8_path(p) && (!w->w1_scale || !w->w2_scale)) return MOE_ERR_INVALID_ARG;
+  if (shared) {
+    if (!shared->w1 || !shared->w2 || !shared->out || !shared->aux_stream || !shared->input_ready ||
+        !shared->output_ready)
+      return MOE_ERR_INVALID_ARG;
+    if (out == x || shared->out == x) return MOE_ERR_INVALID_ARG;
+  }
+  return MOE_OK;
+}
+
+__global__ void copy_status_kernel(const int32_t *__restrict__ from, int32_t *__restrict__ to) { *to = *from; }
+
 }  // namespace
 
 extern "C" {
@@ -420,7 +470,7 @@ const char *moe_status_str(moe_status s) {
   return "unknown status";
 }
 
-int moe_version(void) { return 3; }
+int moe_version(void) { return 4; }
 
 moe_status moe_validate(const moe_problem *p) { return validate(p); }
 
@@ -540,14 +590,7 @@ moe_status moe_forward(const moe_problem *p, const float *logits, const void *x,
   if (p->M == 0) return MOE_OK;
   moe_ws_layout L;
   if ((st = check_ws(*p, workspace, workspace_bytes, L)) != MOE_OK) return st;
-  if (!logits || !x || !w || !w->w1 || !w->w2 || !out) return MOE_ERR_INVALID_ARG;
-  if (fp8_path(*p) && (!w->w1_scale || !w->w2_scale)) return MOE_ERR_INVALID_ARG;
-  if (shared) {
-    if (!shared->w1 || !shared->w2 || !shared->out || !shared->aux_stream || !shared->input_ready ||
-        !shared->output_ready)
-      return MOE_ERR_INVALID_ARG;
-    if (out == x || shared->out == x) return MOE_ERR_INVALID_ARG;
-  }
+  if ((st = forward_args(*p, logits, x, w, out, shared)) != MOE_OK) return st;
   record(events, 0, stream);
   // Shared expert on the aux stream, overlapping the routed path: from the
   // down GEMM on, or from the start when the experts step is chunked.
@@ -596,6 +639,28 @@ moe_status moe_forward(const moe_problem *p, const float *logits, const void *x,
     MOE_HIP(launch_combine(*p, fused, cw, at<int32_t>(workspace, L.inv), !standard, out, stream));
   record(events, 5, stream);
   if (shared) MOE_HIP(hipStreamWaitEvent(stream, shared->output_ready, 0));
+  return MOE_OK;
+}
+
+moe_status moe_forward_noalloc(const moe_problem *p, const float *logits, const void *x,
+                               const moe_weights *w, void *out, const moe_shared *shared,
+                               hipStream_t stream, const moe_stage_events *events, int32_t *status_out) {
+  moe_status st = validate(p);
+  if (st != MOE_OK) return st;
+  if ((shared != nullptr) != (p->shared_N > 0)) return MOE_ERR_INVALID_ARG;
+  if (p->M == 0) return MOE_OK;
+  moe_ws_layout L;
+  layout(*p, L);
+  if (L.total_bytes > (size_t)MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  if ((st = forward_args(*p, logits, x, w, out, shared)) != MOE_OK) return st;
+  void *ws = nullptr;
+  if ((st = static_scratch(stream, &ws)) != MOE_OK) return st;
+  if ((st = moe_forward(p, logits, x, w, out, shared, ws, MOE_STATIC_SCRATCH_BYTES, stream, events)) != MOE_OK)
+    return st;
+  if (status_out) {
+    copy_status_kernel<<<1, 1, 0, stream>>>(at<int32_t>(ws, L.status), status_out);
+    MOE_HIP(hipGetLastError());
+  }
   return MOE_OK;
 }
 

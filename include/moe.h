@@ -197,9 +197,8 @@ typedef struct moe_ws_layout {
 } moe_ws_layout;
 
 const char *moe_status_str(moe_status s);
-/* ABI version, raised whenever a struct or a call changes: 3 (moe_ws_layout
- * gained down_partial and down_split; a caller built against 2 passes a
- * smaller moe_ws_layout to moe_workspace_layout). */
+/* ABI version, raised whenever a struct or a call changes: 4 (3: moe_ws_layout
+ * gained down_partial and down_split; 4: moe_forward_noalloc). */
 int moe_version(void);
 
 /* Host-side check of a problem description (the asserts of
@@ -296,6 +295,29 @@ moe_status moe_forward(const moe_problem *p, const float *logits, const void *x,
                        const moe_weights *w, void *out, const moe_shared *shared,
                        void *workspace, size_t workspace_bytes, hipStream_t stream,
                        const moe_stage_events *events);
+
+/* For callers that cannot allocate device memory (code under hipGraph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): moe_forward
+ * with the workspace held by the library itself, a static device array of
+ * MOE_STATIC_SCRATCH_BYTES on each GPU the library runs on (kept until the
+ * process ends), instead of a caller buffer.  Arguments as moe_forward; the
+ * caller still owns every input and output.  stream must belong to the
+ * current device; the first call on each device looks up that device's copy
+ * of the array (outside graph capture: make one eager call first).
+ *  - MOE_ERR_WORKSPACE when moe_workspace_size() of the problem exceeds
+ *    MOE_STATIC_SCRATCH_BYTES (nothing is launched).
+ *  - status_out (device int32, may be NULL) receives the device status word
+ *    of this call once the stream reaches the end of its work (untouched when
+ *    M == 0).
+ *  - Every call on one GPU shares that GPU's array: calls that overlap on one
+ *    GPU (other streams, other host threads) race and give undefined results;
+ *    calls in one stream order are safe.  Nothing is carried from one call to
+ *    the next (the kernels reset what must start at zero).
+ *  - Allocates nothing: no hipMalloc, hipFree or allocating library call. */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_forward_noalloc(const moe_problem *p, const float *logits, const void *x,
+                               const moe_weights *w, void *out, const moe_shared *shared,
+                               hipStream_t stream, const moe_stage_events *events, int32_t *status_out);
 
 #ifdef __cplusplus
 }

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = moe.load_library()
-    assert L.moe_version() == 3
+    assert L.moe_version() == 4
     assert moe.status_str(moe.MOE_OK) == "ok"
     assert "workspace" in moe.status_str(moe.MOE_ERR_WORKSPACE)
 
@@ -244,3 +244,20 @@ def test_down_gemm_k_split_layout():
     assert ch.down_split in (1, 2)
     if ch.down_split == 2:
         assert ch.total_bytes >= ch.down_partial + 2 * ch.perm_len * wl.K * 4
+
+
+def test_noalloc_forward_rejects_problems_beyond_its_scratch():
+    """moe_forward_noalloc checks the problem's workspace against the static
+    array on the host, before any launch or pointer use."""
+    L = moe.load_library()
+    wl = WORKLOADS["skewed_bf16"]
+    p = moe.make_problem(wl.E, wl.M, 2 * wl.I, wl.K, wl.topk)
+    assert moe.workspace_size(p) > moe.STATIC_SCRATCH_BYTES
+    w = moe.Weights()
+    assert L.moe_forward_noalloc(C.byref(p), None, None, C.byref(w), None, None, None, None, None) == \
+        moe.MOE_ERR_WORKSPACE
+    small = moe.make_problem(8, 64, 256, 256, 2, act_dtype=moe.DTYPE_F32, w_dtype=moe.DTYPE_F32)
+    assert moe.workspace_size(small) <= moe.STATIC_SCRATCH_BYTES
+    # within the limit, the usual argument checks apply (null inputs)
+    assert L.moe_forward_noalloc(C.byref(small), None, None, C.byref(w), None, None, None, None, None) == \
+        moe.MOE_ERR_INVALID_ARG
