@@ -56,6 +56,9 @@ def parse():
                     help="run one expert-parallel shard of this many (expert_map: global expert g is local "
                          "to shard g %% N); routing stays global")
     ap.add_argument("--shard", type=int, default=0, help="which shard with --expert-shards")
+    ap.add_argument("--dbo", action="store_true",
+                    help="run the step as two microbatches (moe_forward_dbo: dispatch and combine on a second "
+                         "stream beside the other microbatch's expert GEMMs)")
     ap.add_argument("--copy-calibration", type=float, default=0.0,
                     help="only run a plain device copy of this many GiB (counter calibration)")
     return ap.parse_args()
@@ -213,6 +216,11 @@ def main():
         pack_ms = a.elapsed_time(b)
     ws = moe.empty_workspace(p)
     L = moe.workspace_layout(p)
+    dbo = None
+    if args.dbo:
+        q = moe.dbo_microbatch_problem(p)
+        dbo = ([moe.empty_workspace(q), moe.empty_workspace(q)], torch.cuda.Stream(), moe.DboEvents())
+        variant["dbo"] = "two microbatches of %d and %d tokens" % ((wl.M + 1) // 2, wl.M // 2)
     odt = torch.float32 if wl.act_dtype == 0 else torch.bfloat16
     out = torch.empty(wl.M, wl.K, dtype=odt, device="cuda")
     shared = streams = None
@@ -221,7 +229,14 @@ def main():
         streams = moe.SharedExpertStreams()
     stream = torch.cuda.current_stream()
 
+    dbo_streams = (moe.SharedExpertStreams(), moe.SharedExpertStreams()) if (dbo and wl.shared_I) else None
+
     def step(events=None):
+        if dbo:
+            # no stage events inside the two-microbatch schedule: whole-step timing only
+            moe.moe_forward_dbo(p, d["logits"], d["x"], gw["w1"], d.get("w1_scale"), gw["w2"], d.get("w2_scale"),
+                                out, dbo[0], dbo[1], dbo[2], stream=stream, shared=shared, shared_streams=dbo_streams)
+            return
         moe.moe_forward(p, d["logits"], d["x"], gw["w1"], d.get("w1_scale"), gw["w2"], d.get("w2_scale"), out, ws,
                         stream=stream, shared=shared, shared_streams=streams, events=events)
 
@@ -250,7 +265,14 @@ def main():
     stage_avg = stage_ms.mean(axis=0)
     gemm1_ms = float(stage_avg[2])
 
-    counts = ws[L.counts: L.counts + 4 * wl.E].view(torch.int32).cpu().numpy()
+    if dbo:
+        # counts of the whole batch = the two microbatches' counts
+        Lq = moe.workspace_layout(moe.dbo_microbatch_problem(p))
+        counts = sum(w_[Lq.counts: Lq.counts + 4 * wl.E].view(torch.int32).cpu().numpy() for w_ in dbo[0][:2])
+        stage_avg = np.full(moe.NUM_STAGE_EVENTS - 1, np.nan)
+        gemm1_ms = float("nan")
+    else:
+        counts = ws[L.counts: L.counts + 4 * wl.E].view(torch.int32).cpu().numpy()
     local_pairs = wl.M * wl.topk * wl.E // wl.global_E if wl.global_E > wl.E else wl.M * wl.topk
     streaming = wl.w_dtype != 0 and local_pairs <= wl.E * (128 if wl.w_dtype == 2 else 256)
     g1_bytes, g1_flops = gemm1_algorithmic(wl, counts)
@@ -268,8 +290,13 @@ def main():
         s.wait_stream(stream)
         with torch.cuda.stream(s):
             with torch.cuda.graph(g, stream=s):
-                moe.moe_forward(p, d["logits"], d["x"], gw["w1"], d.get("w1_scale"), gw["w2"], d.get("w2_scale"),
-                                out, ws, shared=shared, shared_streams=streams)
+                if dbo:
+                    moe.moe_forward_dbo(p, d["logits"], d["x"], gw["w1"], d.get("w1_scale"), gw["w2"],
+                                        d.get("w2_scale"), out, dbo[0], dbo[1], dbo[2], shared=shared,
+                                        shared_streams=dbo_streams)
+                else:
+                    moe.moe_forward(p, d["logits"], d["x"], gw["w1"], d.get("w1_scale"), gw["w2"],
+                                    d.get("w2_scale"), out, ws, shared=shared, shared_streams=streams)
         torch.cuda.synchronize()
         for _ in range(args.warmup):
             g.replay()
@@ -304,6 +331,8 @@ def main():
     if args.chunk_tokens and args.chunk_tokens < wl.M:
         # the stage events mark the last chunk's kernels only: no per-launch roofline
         roofline = {"bound": None, "note": "chunked run: stage events cover the last chunk only"}
+    if dbo:
+        roofline = {"bound": None, "note": "two-microbatch run: no stage events, whole-step timing only"}
     result = {
         # value is the layer's tokens/s; the grouped GEMMs' TFLOP/s and roofline
         # fraction are in gemm_tflops and roofline
@@ -337,7 +366,14 @@ def main():
         "cpu_baseline": cpu,
         "wall_s": wall,
     }
-    print(json.dumps(result), flush=True)
+    def clean(v):
+        # NaN (stages a two-microbatch run does not time) -> null
+        if isinstance(v, dict):
+            return {k: clean(x) for k, x in v.items()}
+        if isinstance(v, float) and v != v:
+            return None
+        return v
+    print(json.dumps(clean(result)), flush=True)
 
 
 if __name__ == "__main__":

@@ -62,6 +62,10 @@ class StageEvents(C.Structure):
     _fields_ = [("ev", C.c_void_p * NUM_STAGE_EVENTS)]
 
 
+class DboEventsStruct(C.Structure):
+    _fields_ = [("prepared", C.c_void_p * 2), ("computed", C.c_void_p * 2), ("finalized", C.c_void_p * 2)]
+
+
 class WsLayout(C.Structure):
     _fields_ = [(n, C.c_size_t) for n in (
         "total_bytes", "status", "counts", "offsets", "chunk_hist", "tiles", "perm", "inv", "act",
@@ -72,10 +76,10 @@ class WsLayout(C.Structure):
 
 EXPORTS = ("moe_status_str", "moe_version", "moe_validate", "moe_workspace_size", "moe_workspace_layout",
            "moe_pack_weights", "moe_route", "moe_prepare", "moe_experts", "moe_finalize", "moe_shared_expert", "moe_forward",
-           "moe_forward_noalloc")
+           "moe_forward_noalloc", "moe_prepare_async", "moe_finalize_async", "moe_receive", "moe_forward_dbo")
 
 _lib = None
-ABI_VERSION = 4   # the struct layouts and calls mirrored here
+ABI_VERSION = 5   # the struct layouts and calls mirrored here
 STATIC_SCRATCH_BYTES = 64 << 20   # MOE_STATIC_SCRATCH_BYTES of moe_forward_noalloc
 
 
@@ -104,6 +108,11 @@ def load_library(path: str = LIB_PATH):
         "moe_shared_expert": [P(Problem), vp, vp, vp, vp, vp, C.c_size_t, vp],
         "moe_forward": [P(Problem), vp, vp, P(Weights), vp, P(Shared), vp, C.c_size_t, vp, P(StageEvents)],
         "moe_forward_noalloc": [P(Problem), vp, vp, P(Weights), vp, P(Shared), vp, P(StageEvents), vp],
+        "moe_prepare_async": [P(Problem), vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp, vp],
+        "moe_finalize_async": [P(Problem), vp, vp, vp, vp, C.c_size_t, vp, vp],
+        "moe_receive": [vp, vp],
+        "moe_forward_dbo": [P(Problem), vp, vp, P(Weights), vp, P(Shared), vp, vp, C.c_size_t, vp, vp,
+                            P(DboEventsStruct)],
     }.items():
         f = getattr(L, name)
         f.restype = C.c_int
@@ -280,3 +289,70 @@ def moe_forward_noalloc(p: Problem, logits, x, w1, w1_scale, w2, w2_scale, out, 
     sh, ev = _shared_and_events(shared, shared_streams, events)
     _check(L.moe_forward_noalloc(C.byref(p), _ptr(logits), _ptr(x), C.byref(w), _ptr(out), sh, _stream(stream),
                                  ev, _ptr(status_out)), "moe_forward_noalloc")
+
+
+# ------------------------------------------- asynchronous prepare / finalize
+
+def moe_prepare_async(p: Problem, x, topk_ids, a_out, a_scale_out, expert_num_tokens, workspace, stream, done,
+                      topk_weights=None):
+    """moe_prepare enqueued on `stream`, `done` (torch.cuda.Event) recorded after it."""
+    wp, wn = _ws(workspace)
+    _check(load_library().moe_prepare_async(C.byref(p), _ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(a_out),
+                                            _ptr(a_scale_out), _ptr(expert_num_tokens), wp, wn, _stream(stream),
+                                            _event_handle(done)), "moe_prepare_async")
+
+
+def moe_finalize_async(p: Problem, fused_out, topk_weights, out, workspace, stream, done):
+    wp, wn = _ws(workspace)
+    _check(load_library().moe_finalize_async(C.byref(p), _ptr(fused_out), _ptr(topk_weights), _ptr(out), wp, wn,
+                                             _stream(stream), _event_handle(done)), "moe_finalize_async")
+
+
+def moe_receive(stream, done):
+    """`stream` waits on the device for the work `done` marks."""
+    _check(load_library().moe_receive(_stream(stream), _event_handle(done)), "moe_receive")
+
+
+class DboEvents:
+    """The six events of moe_forward_dbo."""
+
+    def __init__(self):
+        self.events = [torch.cuda.Event() for _ in range(6)]
+
+    def struct(self) -> DboEventsStruct:
+        h = [_event_handle(e) for e in self.events]
+        return DboEventsStruct((C.c_void_p * 2)(h[0], h[1]), (C.c_void_p * 2)(h[2], h[3]),
+                               (C.c_void_p * 2)(h[4], h[5]))
+
+
+def dbo_microbatch_problem(p: Problem) -> Problem:
+    """The problem each moe_forward_dbo workspace is sized for ((M + 1) / 2 tokens)."""
+    q = Problem.from_buffer_copy(p)
+    q.M = (p.M + 1) // 2
+    return q
+
+
+def moe_forward_dbo(p: Problem, logits, x, w1, w1_scale, w2, w2_scale, out, workspaces, comm_stream,
+                    events: DboEvents, stream=None, shared=None, shared_streams=None):
+    """Two-microbatch layer.  workspaces: two tensors of at least
+    workspace_size(dbo_microbatch_problem(p)) bytes; shared = (w1s, w2s,
+    shared_out) with shared_streams a pair of SharedExpertStreams (one per
+    microbatch)."""
+    L = load_library()
+    w0, n0 = _ws(workspaces[0])
+    w1p, n1 = _ws(workspaces[1])
+    w = _weights(w1, w1_scale, w2, w2_scale)
+    sh = None
+    if shared is not None:
+        if shared_streams is None or len(shared_streams) != 2:
+            raise ValueError("a shared expert needs one SharedExpertStreams per microbatch")
+        w1s, w2s, sout = shared
+        m0 = (p.M + 1) // 2
+        halves = (sout[:m0], sout[m0:])
+        sh = (Shared * 2)(*[Shared(_ptr(w1s), _ptr(w2s), _ptr(halves[u]) if halves[u].numel() else None,
+                                   shared_streams[u].stream.cuda_stream,
+                                   _event_handle(shared_streams[u].input_ready),
+                                   _event_handle(shared_streams[u].output_ready)) for u in range(2)])
+    ev = events.struct()
+    _check(L.moe_forward_dbo(C.byref(p), _ptr(logits), _ptr(x), C.byref(w), _ptr(out), sh, w0, w1p, min(n0, n1),
+                             _stream(stream), _stream(comm_stream), C.byref(ev)), "moe_forward_dbo")

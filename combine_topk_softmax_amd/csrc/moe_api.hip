@@ -453,6 +453,51 @@ moe_status forward_args(const moe_problem &p, const float *logits, const void *x
   return MOE_OK;
 }
 
+// ------------------------------------------- two-microbatch (DBO) schedule
+// The routed layer of one microbatch, in the three parts the two-microbatch
+// schedule puts on different streams: route + prepare (dispatch), the
+// experts, and finalize (combine).
+struct FwdBatch {
+  moe_problem p;              // M = this microbatch's tokens
+  const float *logits;
+  const void *x;
+  void *out;
+  const moe_shared *shared;   // this microbatch's shared-expert streams and events, or null
+  void *ws;
+  moe_ws_layout L;
+  SplitPartials sp;
+};
+
+moe_status fwd_route_prepare(FwdBatch &b, hipStream_t s) {
+  const moe_problem &p = b.p;
+  float *tw = at<float>(b.ws, b.L.topk_weights);
+  int32_t *ti = at<int32_t>(b.ws, b.L.topk_ids);
+  MOE_HIP(launch_route(p, b.logits, tw, ti, s));
+  void *a_q = prepared_rows(p) ? at<void>(b.ws, b.L.a_q) : nullptr;
+  float *a_s = p.act_quant == MOE_QUANT_FP8_TOKEN_GROUP_128 ? at<float>(b.ws, b.L.a_scale) : nullptr;
+  return do_prepare(p, b.x, ti, tw, a_q, a_s, at<int32_t>(b.ws, b.L.counts), b.ws, b.L, s);
+}
+
+moe_status fwd_experts(FwdBatch &b, const moe_weights &w, hipStream_t s) {
+  const moe_problem &p = b.p;
+  void *a_q = prepared_rows(p) ? at<void>(b.ws, b.L.a_q) : nullptr;
+  float *a_s = p.act_quant == MOE_QUANT_FP8_TOKEN_GROUP_128 ? at<float>(b.ws, b.L.a_scale) : nullptr;
+  const SharedStart sh{&b.p, b.x, b.shared, b.ws, &b.L};
+  return do_experts(p, a_q ? a_q : b.x, a_s, w, at<int32_t>(b.ws, b.L.counts), at<void>(b.ws, b.L.fused_out), b.ws,
+                    b.L, s, nullptr, b.shared ? &sh : nullptr, &b.sp);
+}
+
+moe_status fwd_finalize(FwdBatch &b, hipStream_t s) {
+  const moe_problem &p = b.p;
+  const float *cw = p.apply_router_weight_on_input ? nullptr : at<float>(b.ws, b.L.topk_weights);
+  const int32_t *inv = at<int32_t>(b.ws, b.L.inv);
+  if (b.sp.part)
+    MOE_HIP(launch_combine_split(p, b.sp.part, b.sp.S, b.sp.stride, cw, inv, b.out, s));
+  else
+    MOE_HIP(launch_combine(p, at<void>(b.ws, b.L.fused_out), cw, inv, p.format != MOE_FORMAT_STANDARD, b.out, s));
+  return MOE_OK;
+}
+
 __global__ void copy_status_kernel(const int32_t *__restrict__ from, int32_t *__restrict__ to) { *to = *from; }
 
 }  // namespace
@@ -470,7 +515,7 @@ const char *moe_status_str(moe_status s) {
   return "unknown status";
 }
 
-int moe_version(void) { return 4; }
+int moe_version(void) { return 5; }
 
 moe_status moe_validate(const moe_problem *p) { return validate(p); }
 
@@ -661,6 +706,94 @@ moe_status moe_forward_noalloc(const moe_problem *p, const float *logits, const 
     copy_status_kernel<<<1, 1, 0, stream>>>(at<int32_t>(ws, L.status), status_out);
     MOE_HIP(hipGetLastError());
   }
+  return MOE_OK;
+}
+
+moe_status moe_prepare_async(const moe_problem *p, const void *x, const int32_t *topk_ids,
+                             const float *topk_weights, void *a_out, float *a_scale_out,
+                             int32_t *expert_num_tokens, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream, hipEvent_t done) {
+  if (!done) return MOE_ERR_INVALID_ARG;
+  const moe_status st = moe_prepare(p, x, topk_ids, topk_weights, a_out, a_scale_out, expert_num_tokens, workspace,
+                                    workspace_bytes, stream);
+  if (st != MOE_OK) return st;
+  MOE_HIP(hipEventRecord(done, stream));
+  return MOE_OK;
+}
+
+moe_status moe_finalize_async(const moe_problem *p, const void *fused_out, const float *topk_weights,
+                              void *out, void *workspace, size_t workspace_bytes, hipStream_t stream,
+                              hipEvent_t done) {
+  if (!done) return MOE_ERR_INVALID_ARG;
+  const moe_status st = moe_finalize(p, fused_out, topk_weights, out, workspace, workspace_bytes, stream);
+  if (st != MOE_OK) return st;
+  MOE_HIP(hipEventRecord(done, stream));
+  return MOE_OK;
+}
+
+moe_status moe_receive(hipStream_t stream, hipEvent_t done) {
+  if (!done) return MOE_ERR_INVALID_ARG;
+  MOE_HIP(hipStreamWaitEvent(stream, done, 0));
+  return MOE_OK;
+}
+
+moe_status moe_forward_dbo(const moe_problem *p, const float *logits, const void *x, const moe_weights *w,
+                           void *out, const moe_shared *shared, void *workspace0, void *workspace1,
+                           size_t workspace_bytes, hipStream_t compute_stream, hipStream_t comm_stream,
+                           const moe_dbo_events *ev) {
+  moe_status st = validate(p);
+  if (st != MOE_OK) return st;
+  if ((shared != nullptr) != (p->shared_N > 0)) return MOE_ERR_INVALID_ARG;
+  if (chunked(*p)) return MOE_ERR_UNSUPPORTED;
+  if (p->M == 0) return MOE_OK;
+  if (!ev) return MOE_ERR_INVALID_ARG;
+  for (int u = 0; u < 2; ++u)
+    if (!ev->prepared[u] || !ev->computed[u] || !ev->finalized[u]) return MOE_ERR_INVALID_ARG;
+  if (!logits || !x || !out) return MOE_ERR_INVALID_ARG;
+  // microbatch 0: the first (M + 1) / 2 tokens, microbatch 1: the rest
+  const int64_t Mu[2] = {(p->M + 1) / 2, p->M / 2};
+  const int64_t row_bytes = p->K * act_elem_bytes(p->act_dtype);
+  void *ws[2] = {workspace0, workspace1};
+  FwdBatch b[2];
+  const int nb = Mu[1] > 0 ? 2 : 1;
+  for (int u = 0; u < nb; ++u) {
+    const int64_t m0 = u == 0 ? 0 : Mu[0];
+    b[u].p = *p;
+    b[u].p.M = Mu[u];
+    b[u].logits = logits + m0 * router_width(*p);
+    b[u].x = reinterpret_cast<const uint8_t *>(x) + m0 * row_bytes;
+    b[u].out = reinterpret_cast<uint8_t *>(out) + m0 * row_bytes;
+    b[u].shared = shared ? &shared[u] : nullptr;
+    b[u].ws = ws[u];
+    if ((st = check_ws(b[u].p, ws[u], workspace_bytes, b[u].L)) != MOE_OK) return st;
+    if ((st = forward_args(b[u].p, b[u].logits, b[u].x, w, b[u].out, b[u].shared)) != MOE_OK) return st;
+  }
+  if (nb == 2 && workspace0 == workspace1) return MOE_ERR_INVALID_ARG;
+  // The comm stream starts from the compute stream's position.
+  MOE_HIP(hipEventRecord(ev->finalized[1], compute_stream));
+  MOE_HIP(hipStreamWaitEvent(comm_stream, ev->finalized[1], 0));
+  // Dispatch side: both microbatches' route + prepare, back to back; the
+  // second overlaps the first one's expert GEMMs.
+  for (int u = 0; u < nb; ++u) {
+    if ((st = fwd_route_prepare(b[u], comm_stream)) != MOE_OK) return st;
+    MOE_HIP(hipEventRecord(ev->prepared[u], comm_stream));
+  }
+  // Compute side: each microbatch's experts once its dispatch is in; the
+  // combine of microbatch 0 runs on the comm stream beside microbatch 1's
+  // experts.
+  for (int u = 0; u < nb; ++u) {
+    MOE_HIP(hipStreamWaitEvent(compute_stream, ev->prepared[u], 0));
+    if ((st = fwd_experts(b[u], *w, compute_stream)) != MOE_OK) return st;
+    MOE_HIP(hipEventRecord(ev->computed[u], compute_stream));
+    MOE_HIP(hipStreamWaitEvent(comm_stream, ev->computed[u], 0));
+    if ((st = fwd_finalize(b[u], comm_stream)) != MOE_OK) return st;
+    MOE_HIP(hipEventRecord(ev->finalized[u], comm_stream));
+  }
+  // Join: the compute stream passes the end once every combine (and shared
+  // expert) is done.
+  MOE_HIP(hipStreamWaitEvent(compute_stream, ev->finalized[nb - 1], 0));
+  for (int u = 0; u < nb; ++u)
+    if (b[u].shared) MOE_HIP(hipStreamWaitEvent(compute_stream, b[u].shared->output_ready, 0));
   return MOE_OK;
 }
 

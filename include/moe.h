@@ -197,8 +197,9 @@ typedef struct moe_ws_layout {
 } moe_ws_layout;
 
 const char *moe_status_str(moe_status s);
-/* ABI version, raised whenever a struct or a call changes: 4 (3: moe_ws_layout
- * gained down_partial and down_split; 4: moe_forward_noalloc). */
+/* ABI version, raised whenever a struct or a call changes: 5 (3: moe_ws_layout
+ * gained down_partial and down_split; 4: moe_forward_noalloc; 5: the
+ * asynchronous prepare / finalize calls and moe_forward_dbo). */
 int moe_version(void);
 
 /* Host-side check of a problem description (the asserts of
@@ -295,6 +296,70 @@ moe_status moe_forward(const moe_problem *p, const float *logits, const void *x,
                        const moe_weights *w, void *out, const moe_shared *shared,
                        void *workspace, size_t workspace_bytes, hipStream_t stream,
                        const moe_stage_events *events);
+
+/* ---------------------------------------------------------------------
+ * Asynchronous prepare / finalize and the two-microbatch schedule
+ * (modular_kernel.py page: FusedMoEPrepareAndFinalize.prepare_async and
+ * finalize_async, whose result is a hook / receiver pair equivalent to
+ * prepare / finalize; FusedMoEModularKernel.shared_buffers, one set of
+ * buffers per DBO microbatch; the supports_async() branch of
+ * FusedMoEModularKernel.forward; page "DBO HT without cudagraph").  On one
+ * GPU the dispatch and combine are local kernels, so what the overlap can
+ * hide is their latency-bound chain (router, counting, scan, ranking), not
+ * communication.
+ */
+
+/* moe_prepare enqueued on `stream` (the dispatch stream), then `done`
+ * recorded there; returns at once.  The outputs are valid on any stream once
+ * it has passed moe_receive(that stream, done) (or done has completed); until
+ * then they must not be read.  Same arguments and errors as moe_prepare;
+ * `done` must be a valid event. */
+moe_status moe_prepare_async(const moe_problem *p, const void *x, const int32_t *topk_ids,
+                             const float *topk_weights, void *a_out, float *a_scale_out,
+                             int32_t *expert_num_tokens, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream, hipEvent_t done);
+
+/* moe_finalize enqueued on `stream`, then `done` recorded there; out is valid
+ * after moe_receive(consumer, done).  Same arguments and errors as
+ * moe_finalize. */
+moe_status moe_finalize_async(const moe_problem *p, const void *fused_out, const float *topk_weights,
+                              void *out, void *workspace, size_t workspace_bytes, hipStream_t stream,
+                              hipEvent_t done);
+
+/* The receiver: `stream` waits (on the device, the host returns at once) for
+ * the work `done` marks.  hipEventQuery(done) is the non-blocking check. */
+moe_status moe_receive(hipStream_t stream, hipEvent_t done);
+
+/* Events of moe_forward_dbo, created by the caller (any flags). */
+typedef struct moe_dbo_events {
+  hipEvent_t prepared[2];   /* dispatch stream: microbatch u routed and prepared */
+  hipEvent_t computed[2];   /* compute stream: microbatch u's expert GEMMs done  */
+  hipEvent_t finalized[2];  /* dispatch stream: microbatch u combined            */
+} moe_dbo_events;
+
+/* The layer in two microbatches (tokens [0, (M+1)/2) and [(M+1)/2, M)), each
+ * with its own workspace, on two streams:
+ *   dispatch stream: route + prepare of microbatch 0, then of microbatch 1
+ *                    (beside microbatch 0's expert GEMMs), then each
+ *                    microbatch's combine once its experts are done (the
+ *                    combine of 0 beside the experts of 1);
+ *   compute stream:  the expert GEMMs of microbatch 0, then of microbatch 1.
+ * The dispatch stream starts from the compute stream's position at the call
+ * and the compute stream joins it at the end, so to the caller this is one
+ * call on compute_stream, like moe_forward; out [M, K] is fully written.
+ * Each token's result equals moe_forward's whenever both pick the same GEMM
+ * kernels (the microbatches are half as large, which can change the choice).
+ *  - workspace0 / workspace1: distinct, each at least moe_workspace_size() of
+ *    the problem with M replaced by (M + 1) / 2.
+ *  - shared: NULL, or an array of two moe_shared, one per microbatch (its
+ *    rows of the shared output and its own event pair, as the SharedExperts
+ *    page keeps one pair per microbatch).
+ *  - MOE_ERR_UNSUPPORTED with chunk_tokens > 0 (chunk the microbatches
+ *    instead). */
+moe_status moe_forward_dbo(const moe_problem *p, const float *logits, const void *x, const moe_weights *w,
+                           void *out, const moe_shared *shared, void *workspace0, void *workspace1,
+                           size_t workspace_bytes, hipStream_t compute_stream, hipStream_t comm_stream,
+                           const moe_dbo_events *ev);
 
 /* For callers that cannot allocate device memory (code under hipGraph
  * capture, tight serving loops, harnesses that forbid hipMalloc): moe_forward

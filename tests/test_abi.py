@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     L = moe.load_library()
-    assert L.moe_version() == 4
+    assert L.moe_version() == 5
     assert moe.status_str(moe.MOE_OK) == "ok"
     assert "workspace" in moe.status_str(moe.MOE_ERR_WORKSPACE)
 
@@ -261,3 +261,25 @@ def test_noalloc_forward_rejects_problems_beyond_its_scratch():
     # within the limit, the usual argument checks apply (null inputs)
     assert L.moe_forward_noalloc(C.byref(small), None, None, C.byref(w), None, None, None, None, None) == \
         moe.MOE_ERR_INVALID_ARG
+
+
+def test_dbo_forward_host_checks():
+    """moe_forward_dbo refuses, before any launch: one workspace for both
+    microbatches, a workspace smaller than a microbatch's, chunking, and
+    missing events."""
+    L = moe.load_library()
+    p = moe.make_problem(8, 64, 256, 256, 2, act_dtype=moe.DTYPE_F32, w_dtype=moe.DTYPE_F32)
+    q = moe.dbo_microbatch_problem(p)
+    assert q.M == 32 and p.M == 64
+    need = moe.workspace_size(q)
+    assert need < moe.workspace_size(p)
+    w = moe.Weights(1, None, 2, None)
+    ev = moe.DboEventsStruct((C.c_void_p * 2)(1, 2), (C.c_void_p * 2)(3, 4), (C.c_void_p * 2)(5, 6))
+    args = lambda ws0, ws1, n, e: (C.byref(p), 8, 16, C.byref(w), 24, None, ws0, ws1, n, None, None, e)
+    assert L.moe_forward_dbo(*args(4096, 4096, need, C.byref(ev))) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_forward_dbo(*args(4096, 8192, need - 1, C.byref(ev))) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_forward_dbo(*args(4096, 8192, need, None)) == moe.MOE_ERR_INVALID_ARG
+    pc = moe.Problem.from_buffer_copy(p)
+    pc.chunk_tokens = 16
+    assert L.moe_forward_dbo(C.byref(pc), 8, 16, C.byref(w), 24, None, 4096, 8192, need, None, None,
+                             C.byref(ev)) == moe.MOE_ERR_UNSUPPORTED

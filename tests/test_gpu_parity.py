@@ -980,3 +980,137 @@ def test_forward_random_shapes(name, wl):
     err = U.rel_err(out.float().cpu().numpy(), ref)
     print(f"  {name}: max rel err {err:.3e}", flush=True)
     assert err <= U.tol_for(wl)
+
+
+# ------------------------------- asynchronous prepare / finalize, two microbatches
+
+def test_async_prepare_finalize_equal_the_stage_calls():
+    """prepare_async / finalize_async on a dispatch stream, received on the
+    compute stream, give exactly what the synchronous stage calls give (the
+    hook / receiver pair is equivalent to prepare / finalize)."""
+    for wl in (SMALL["bf16_ragged"], SMALL["fp8_batched"], SMALL["bf16_split_k"]):
+        d = U.to_cuda(make_inputs(wl, seed=33, device="cpu"))
+        ref, _, _, p = U.run_forward(wl, d)
+        ws = moe.empty_workspace(p)
+        w = torch.empty(wl.M, wl.topk, device="cuda")
+        ids = torch.empty(wl.M, wl.topk, dtype=torch.int32, device="cuda")
+        moe.moe_route(p, d["logits"], w, ids)
+        fp8 = wl.act_quant == QUANT_FP8_G128
+        bat = U.batched(wl)
+        counts = torch.full((wl.E,), -1, dtype=torch.int32, device="cuda")
+        a_out = a_s = None
+        if bat:
+            a_out = torch.empty(wl.E, wl.capacity, wl.K, dtype=torch.uint8 if fp8 else torch.bfloat16, device="cuda")
+            if fp8:
+                a_s = torch.empty(wl.E * wl.capacity, wl.K // 128, device="cuda")
+        comm = torch.cuda.Stream()
+        comm.wait_stream(torch.cuda.current_stream())
+        prepared, combined = torch.cuda.Event(), torch.cuda.Event()
+        moe.moe_prepare_async(p, d["x"], ids, a_out, a_s, counts, ws, comm, prepared)
+        moe.moe_receive(torch.cuda.current_stream(), prepared)
+        rows = wl.E * wl.capacity if bat else wl.M * wl.topk
+        fused = torch.empty(rows, wl.K, dtype=torch.bfloat16, device="cuda")
+        moe.moe_experts(p, a_out if bat else d["x"], a_s, d["w1"], d.get("w1_scale"), d["w2"], d.get("w2_scale"),
+                        counts, fused, ws)
+        out = torch.empty_like(ref)
+        comm.wait_stream(torch.cuda.current_stream())
+        moe.moe_finalize_async(p, fused, w, out, ws, comm, combined)
+        moe.moe_receive(torch.cuda.current_stream(), combined)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+
+
+DBO_CASES = {
+    # the same GEMM kernels for the batch and its halves: bitwise equal to moe_forward
+    "fp8_batched": (WORKLOADS["decode_fp8_m64"].replace(M=96, K=512, I=256, E=16, topk=4, capacity=96), True),
+    "bf16_split_k": (SMALL["bf16_split_k"], True),
+    "bf16_mfma": (SMALL["bf16_mfma_groups"], True),
+    "bf16_shared": (WORKLOADS["dsv3_bf16"].replace(M=256, E=32, I=256, K=512, shared_I=256), True),
+    "odd_M": (SMALL["bf16_ragged"].replace(M=301), True),
+    "M1": (SMALL["bf16_ragged"].replace(M=1), True),
+    # halves of 300 rows per expert stream where the batch takes MFMA tiles:
+    # within the bar of the oracle
+    "bf16_mfma_to_stream": (WORKLOADS["mixtral_bf16"].replace(M=600, K=512, I=256, E=4, topk=2, renormalize=False,
+                                                              logits_dist="normal"), False),
+}
+
+
+def _run_dbo(wl, d, p=None, wss=None, out=None, sout=None, comm=None, events=None, streams=None):
+    p = p or U.problem(wl)
+    if wss is None:
+        q = moe.dbo_microbatch_problem(p)
+        wss = [moe.empty_workspace(q), moe.empty_workspace(q)]
+    out = out if out is not None else torch.empty(wl.M, wl.K, dtype=U.torch_act_dtype(wl), device="cuda")
+    comm = comm or torch.cuda.Stream()
+    events = events or moe.DboEvents()
+    shared = None
+    if wl.shared_I:
+        sout = sout if sout is not None else torch.empty_like(out)
+        streams = streams or (moe.SharedExpertStreams(), moe.SharedExpertStreams())
+        shared = (d["w1s"], d["w2s"], sout)
+    moe.moe_forward_dbo(p, d["logits"], d["x"], d["w1"], d.get("w1_scale"), d["w2"], d.get("w2_scale"), out, wss,
+                        comm, events, shared=shared, shared_streams=streams)
+    return out, sout, wss
+
+
+@pytest.mark.parametrize("name", list(DBO_CASES))
+def test_dbo_forward(name):
+    """moe_forward_dbo (two microbatches, dispatch and combine on a second
+    stream) against moe_forward, and against the oracle."""
+    wl, bitwise = DBO_CASES[name]
+    d = make_inputs(wl, seed=34, device="cpu")
+    g = U.to_cuda(d)
+    ref, sref, _, p = U.run_forward(wl, g)
+    out, sout, wss = _run_dbo(wl, g, p=p)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    assert np.all(np.isfinite(got))
+    if bitwise:
+        assert torch.equal(out, ref)
+        if wl.shared_I:
+            assert torch.equal(sout, sref)
+    toks = sample_tokens(wl.M, 24, seed=6)
+    oref, _, _ = oracle.moe_tokens(wl, d, toks)
+    err = U.rel_err(got[toks], oref)
+    print(f"  dbo {name}: max rel err {err:.3e}", flush=True)
+    assert err <= U.tol_for(wl)
+    # each microbatch's status word is clear
+    q = moe.dbo_microbatch_problem(p)
+    for ws in wss[: 2 if wl.M > 1 else 1]:
+        assert U.ws_view(ws, moe.workspace_layout(q).status, 1).item() == 0
+
+
+def test_dbo_graph_replay_matches_eager():
+    """The two-microbatch layer captured in one graph (the dispatch stream and
+    the shared expert's aux streams fork from and join the capture stream);
+    every replay with fresh inputs is bitwise equal to an eager run."""
+    wl = DBO_CASES["bf16_shared"][0]
+    d = U.to_cuda(make_inputs(wl, seed=35, device="cpu"))
+    p = U.problem(wl)
+    q = moe.dbo_microbatch_problem(p)
+    wss = [moe.empty_workspace(q), moe.empty_workspace(q)]
+    out = torch.empty(wl.M, wl.K, dtype=torch.bfloat16, device="cuda")
+    sout = torch.empty_like(out)
+    comm, events = torch.cuda.Stream(), moe.DboEvents()
+    streams = (moe.SharedExpertStreams(), moe.SharedExpertStreams())
+    _run_dbo(wl, d, p, wss, out, sout, comm, events, streams)   # warm-up
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            _run_dbo(wl, d, p, wss, out, sout, comm, events, streams)
+    torch.cuda.synchronize()
+    for r in range(3):
+        fresh = make_inputs(wl, seed=36 + r, device="cpu")
+        d["logits"].copy_(fresh["logits"].cuda())
+        d["x"].copy_(fresh["x"].cuda())
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got, sgot = out.clone(), sout.clone()
+        ref, sref, _ = _run_dbo(wl, d, p)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), r
+        assert torch.equal(sgot, sref), r
