@@ -162,11 +162,13 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t *__restrict__ id
 
 // --------------------------------------------------- row quantise / scatter
 
-// One block (256 threads = 16 teams of 16 lanes) per token row of x.  A team
+// Blocks of 256 threads = 16 teams of 16 lanes; block (m, y) handles groups
+// y * 16 + team (+ multiples of 16 * gridDim.y) of token row m.  A team
 // handles one group of 128 channels, 8 per lane: |max| by shuffles inside the
 // team, scale, codes.  Each row is read once and written to every destination
 // row: the rows inv[] names for its topk pairs (batched), or row m (standard
-// quantise).
+// quantise).  Spreading a row's groups over blocks keeps the latency chain of
+// a decode batch (few rows) short: one load-quantise-store round per block.
 // With topk_w (router weight on the input, topk == 1) the row is first
 // multiplied by the token's weight and rounded to the activation type.
 template <typename TIn, bool QUANT>
@@ -178,7 +180,7 @@ __global__ __launch_bounds__(256) void dispatch_rows_kernel(const TIn *__restric
   const int m = blockIdx.x;
   const int team = threadIdx.x >> 4, tl = threadIdx.x & 15;
   const int G = K / 128;
-  for (int g = team; g < G; g += 16) {
+  for (int g = blockIdx.y * 16 + team; g < G; g += 16 * gridDim.y) {
     const int c0 = g * 128 + tl * 8;
     float v[8];
     if constexpr (sizeof(TIn) == 2) {
@@ -329,6 +331,136 @@ __global__ __launch_bounds__(1024) void plan_tiles_kernel(const int32_t *__restr
   if (e == 0) tiles[(int64_t)max_tiles * 4] = min(total_sh, max_tiles);
 }
 
+// -------------------------------------------------- small batches, one block
+// Counting, scan, stable ranking and (optionally) the tile plan of a batch of
+// at most kSmallPairs pairs over at most kSmallExperts local experts in one
+// workgroup of 1024 threads, instead of four launches (decode batches spend
+// more time between those launches than in them).  Same outputs as
+// chunk_hist + scan + rank + plan_tiles: each of the 16 wavefronts takes a
+// contiguous run of pairs, the per-wavefront histograms are prefix-summed in
+// wavefront order, and each wavefront ranks its run 64 pairs at a time with
+// ballots, so every expert segment is in ascending pair order.
+constexpr int kSmallPairs = 4096;
+constexpr int kSmallExperts = 256;
+
+__global__ __launch_bounds__(1024) void prepare_small_kernel(
+    const int32_t *__restrict__ ids, int n, int E, int Eg, const int32_t *__restrict__ map, int nbits,
+    int standard, int align, int64_t cap, int32_t *counts, int32_t *expert_num_tokens,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ perm, int64_t perm_len, int32_t *__restrict__ inv,
+    int32_t *__restrict__ status, int clear_status, int tile_rows, int max_tiles, int32_t *__restrict__ tiles) {
+  __shared__ int lid[kSmallPairs];
+  __shared__ int whist[16][kSmallExperts];
+  __shared__ int start_sh[kSmallExperts];
+  __shared__ int total_sh;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (tid == 0 && clear_status) *status = 0;
+  for (int i = tid; i < 16 * kSmallExperts; i += 1024) (&whist[0][0])[i] = 0;
+  __syncthreads();
+  // pairs [w * run, (w + 1) * run) belong to wavefront w
+  const int run = (n + 15) / 16;
+  for (int f = tid; f < n; f += 1024) {
+    const int e = local_expert(ids[f], Eg, map, E);
+    lid[f] = e;
+    if (e < 0) {
+      inv[f] = -1;                                   // another shard's pick, or invalid
+      if (e == -2) atomicOr(status, MOE_DEVICE_BAD_EXPERT_ID);
+    } else {
+      atomicAdd(&whist[f / run][e], 1);
+    }
+  }
+  __syncthreads();
+  // per expert: counts, the wavefronts' prefixes, padded segment offsets
+  int cnt = 0;
+  if (tid < E) {
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      const int h = whist[w][tid];
+      whist[w][tid] = cnt;
+      cnt += h;
+    }
+    counts[tid] = cnt;
+    expert_num_tokens[tid] = cnt;
+  }
+  const int padded = tid < E ? (standard ? (cnt + align - 1) / align * align : 0) : 0;
+  const int start = block_exclusive_scan(padded, &total_sh);
+  if (tid < E) start_sh[tid] = standard ? start : 0;
+  if (standard) {
+    if (tid < E) {
+      offsets[tid] = start;
+      for (int sl = start + cnt; sl < start + padded; ++sl) perm[sl] = -1;
+    }
+    if (tid == 0) offsets[E] = total_sh;
+    for (int64_t sl = total_sh + tid; sl < perm_len; sl += 1024) perm[sl] = -1;
+  }
+  __syncthreads();
+  // stable ranks: wavefront wv walks its run of pairs 64 at a time
+  for (int e = lane; e < E; e += 64) whist[wv][e] += start_sh[e];
+  __syncthreads();
+  const int f0 = wv * run, f1 = min(n, f0 + run);
+  for (int base = f0; base < f1; base += 64) {
+    const int f = base + lane;
+    const int e = f < f1 ? lid[f] : -1;
+    const bool good = e >= 0;
+    uint64_t peers = __ballot(good);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = good && ((e >> b) & 1);
+      const uint64_t bal = __ballot(bit);
+      peers &= bit ? bal : ~bal;
+    }
+    if (good) {
+      const int pos = whist[wv][e] + __popcll(peers & lanemask_lt());
+      if (standard) {
+        perm[pos] = f;
+        inv[f] = pos;
+      } else if (pos < cap) {
+        inv[f] = (int32_t)(e * cap + pos);
+      } else {
+        inv[f] = -1;
+        atomicOr(status, MOE_DEVICE_CAPACITY_OVERFLOW);
+      }
+    }
+    // every lane has read its run position before the leader of each expert
+    // group moves it on (the wavefront executes in lockstep)
+    __builtin_amdgcn_wave_barrier();
+    if (good && (peers & lanemask_lt()) == 0) whist[wv][e] += __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+  }
+  if (tile_rows <= 0) return;   // uniform
+  // tile plan, as plan_tiles_kernel
+  int c = cnt;
+  int64_t seg = 0;
+  if (tid < E) {
+    if (standard) {
+      seg = start;
+      const int64_t room = perm_len - seg;
+      if ((int64_t)c > room) c = (int)max<int64_t>(room, 0);
+    } else {
+      seg = (int64_t)tid * cap;
+      if ((int64_t)c > cap) {
+        c = (int)cap;
+        atomicOr(status, MOE_DEVICE_CAPACITY_OVERFLOW);
+      }
+    }
+  }
+  const int nt = tid < E ? (c + tile_rows - 1) / tile_rows : 0;
+  const int t0 = block_exclusive_scan(nt, &total_sh);
+  if (tid < E) {
+    for (int i = 0; i < nt; ++i) {
+      const int t = t0 + i;
+      if (t >= max_tiles) {
+        atomicOr(status, MOE_DEVICE_CAPACITY_OVERFLOW);
+        break;
+      }
+      int32_t *d = tiles + (int64_t)t * 4;
+      d[0] = tid;
+      d[1] = (int32_t)seg;
+      d[2] = i * tile_rows;
+      d[3] = min(tile_rows, c - i * tile_rows);
+    }
+  }
+  if (tid == 0) tiles[(int64_t)max_tiles * 4] = min(total_sh, max_tiles);
+}
+
 int ceil_log2(int v) {
   int b = 0;
   while ((1 << b) < v) ++b;
@@ -337,12 +469,21 @@ int ceil_log2(int v) {
 
 }  // namespace
 
+bool count_fused(const moe_problem &p) { return p.M * p.topk <= kSmallPairs && p.E <= kSmallExperts; }
+
 hipError_t launch_count_and_permute(const moe_problem &p, const int32_t *ids,
                                     int32_t *expert_num_tokens, const DispatchBufs &b,
                                     hipStream_t s) {
   const int n = (int)(p.M * p.topk), E = (int)p.E, Eg = (int)router_width(p);
   const int standard = p.format == MOE_FORMAT_STANDARD;
   const int align = p.align > 0 ? (int)p.align : 1;
+  if (count_fused(p)) {
+    prepare_small_kernel<<<1, 1024, 0, s>>>(ids, n, E, Eg, p.expert_map, ceil_log2(E), standard, align,
+                                            p.max_tokens_per_expert, b.counts, expert_num_tokens, b.offsets, b.perm,
+                                            b.perm_len, b.inv, b.status, b.clear_status, b.plan_rows, b.max_tiles,
+                                            b.tiles);
+    return hipGetLastError();
+  }
   chunk_hist_kernel<<<(unsigned)b.n_chunks, 256, 0, s>>>(ids, n, E, Eg, p.expert_map, (int)b.chunk,
                                                           b.chunk_hist);
   hipError_t err = hipGetLastError();
@@ -363,7 +504,10 @@ hipError_t launch_dispatch_rows(const moe_problem &p, const void *x, const int32
   const int K = (int)p.K, k = (int)p.topk;
   const bool quant = p.act_quant == MOE_QUANT_FP8_TOKEN_GROUP_128;
   const int32_t *d = batched ? inv : nullptr;
-  dim3 grid((unsigned)p.M), block(256);
+  // enough blocks for every group of a small batch to go at once
+  const int G = K / 128;
+  const int ny = p.M >= 1024 ? 1 : (G + 15) / 16;
+  dim3 grid((unsigned)p.M, (unsigned)ny), block(256);
   if (p.act_dtype == MOE_DTYPE_BF16) {
     if (quant)
       dispatch_rows_kernel<uint16_t, true><<<grid, block, 0, s>>>((const uint16_t *)x, K, k, d, topk_w, a_out, a_scale_out);

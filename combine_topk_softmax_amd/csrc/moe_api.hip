@@ -182,10 +182,27 @@ bool prepared_rows(const moe_problem &p) {
          p.apply_router_weight_on_input;
 }
 
+// Rows per tile of the grouped GEMMs' plan: the streaming kernels' (wide
+// fp8 panels take shorter tiles), the 256-row MFMA tiles, or the general
+// kernel's.
+int gemm_tile_rows(const moe_problem &p, const moe_ws_layout &L) {
+  const int64_t I = p.N / 2;
+  const int64_t local_pairs = local_pairs_of(p, p.M * p.topk);
+  const bool streaming = streaming_of(p, local_pairs);
+  const bool big = !streaming && mfma_gemm_fits(p.w_dtype, p.act_dtype, p.K, I);
+  const bool wide = streaming && stream_gemm_gated_wide(p.w_dtype, p.E, local_pairs, p.K, I);
+  return wide ? stream_gemm_wide_tile_rows() : streaming ? stream_gemm_tile_rows(p.w_dtype)
+                                             : big       ? mfma_gemm_tile_rows()
+                                                         : (int)L.tile_rows;
+}
+
 // Counts and permutation of p.M tokens' pairs (ids), their pair -> slot map
-// written from inv_pair0 on (a chunk's pairs within the batch's map).
+// written from inv_pair0 on (a chunk's pairs within the batch's map).  With
+// plan set, small batches also get the GEMMs' tile plan from the same
+// kernel; returns through *planned whether they did.
 moe_status do_count(const moe_problem &p, const int32_t *ids, int32_t *expert_num_tokens, void *ws,
-                    const moe_ws_layout &L, int64_t inv_pair0, hipStream_t s) {
+                    const moe_ws_layout &L, int64_t inv_pair0, hipStream_t s, bool plan = false,
+                    bool *planned = nullptr) {
   DispatchBufs b;
   b.status = at<int32_t>(ws, L.status);
   b.counts = at<int32_t>(ws, L.counts);
@@ -197,7 +214,11 @@ moe_status do_count(const moe_problem &p, const int32_t *ids, int32_t *expert_nu
   b.n_chunks = L.n_chunks;
   b.chunk = L.chunk;
   b.clear_status = inv_pair0 == 0;
+  b.tiles = at<int32_t>(ws, L.tiles);
+  b.max_tiles = (int)L.max_tiles;
+  b.plan_rows = plan && count_fused(p) ? gemm_tile_rows(p, L) : 0;
   MOE_HIP(launch_count_and_permute(p, ids, expert_num_tokens, b, s));
+  if (planned) *planned = b.plan_rows > 0;
   return MOE_OK;
 }
 
@@ -214,8 +235,8 @@ moe_status do_rows(const moe_problem &p, const void *x, const float *topk_w, voi
 
 moe_status do_prepare(const moe_problem &p, const void *x, const int32_t *ids, const float *topk_w,
                       void *a_out, float *a_scale_out, int32_t *expert_num_tokens, void *ws,
-                      const moe_ws_layout &L, hipStream_t s) {
-  moe_status st = do_count(p, ids, expert_num_tokens, ws, L, 0, s);
+                      const moe_ws_layout &L, hipStream_t s, bool plan = false, bool *planned = nullptr) {
+  moe_status st = do_count(p, ids, expert_num_tokens, ws, L, 0, s, plan, planned);
   if (st != MOE_OK) return st;
   return do_rows(p, x, topk_w, a_out, a_scale_out, ws, L, s);
 }
@@ -258,7 +279,7 @@ struct SplitPartials {
 moe_status do_experts(const moe_problem &p, const void *a, const float *a_scale, const moe_weights &w,
                       const int32_t *counts, void *fused_out, void *ws, const moe_ws_layout &L,
                       hipStream_t s, const moe_stage_events *ev, const SharedStart *sh = nullptr,
-                      SplitPartials *sp = nullptr) {
+                      SplitPartials *sp = nullptr, bool planned = false) {
   const bool standard = p.format == MOE_FORMAT_STANDARD;
   const bool fp8 = fp8_path(p);
   const int64_t I = p.N / 2;
@@ -271,12 +292,10 @@ moe_status do_experts(const moe_problem &p, const void *a, const float *a_scale,
   // where the shapes allow, the general 128 x 128 kernel otherwise.
   const bool big = !streaming && mfma_gemm_fits(p.w_dtype, p.act_dtype, p.K, I);
   const bool wide = streaming && stream_gemm_gated_wide(p.w_dtype, p.E, local_pairs, p.K, I);
-  const int tile_rows = wide        ? stream_gemm_wide_tile_rows()
-                        : streaming ? stream_gemm_tile_rows(p.w_dtype)
-                        : big       ? mfma_gemm_tile_rows()
-                                    : (int)L.tile_rows;
-  MOE_HIP(launch_plan_tiles(p, counts, at<int32_t>(ws, L.offsets), L.perm_len, tile_rows,
-                            (int)L.max_tiles, tiles, status, s));
+  // (a small batch's counting kernel already wrote the plan)
+  if (!planned)
+    MOE_HIP(launch_plan_tiles(p, counts, at<int32_t>(ws, L.offsets), L.perm_len, gemm_tile_rows(p, L),
+                              (int)L.max_tiles, tiles, status, s));
   record(ev, 2, s);
   GemmTiles gt;
   gt.tiles = tiles;
@@ -466,6 +485,7 @@ struct FwdBatch {
   void *ws;
   moe_ws_layout L;
   SplitPartials sp;
+  bool planned = false;       // the counting kernel wrote the tile plan
 };
 
 moe_status fwd_route_prepare(FwdBatch &b, hipStream_t s) {
@@ -475,7 +495,7 @@ moe_status fwd_route_prepare(FwdBatch &b, hipStream_t s) {
   MOE_HIP(launch_route(p, b.logits, tw, ti, s));
   void *a_q = prepared_rows(p) ? at<void>(b.ws, b.L.a_q) : nullptr;
   float *a_s = p.act_quant == MOE_QUANT_FP8_TOKEN_GROUP_128 ? at<float>(b.ws, b.L.a_scale) : nullptr;
-  return do_prepare(p, b.x, ti, tw, a_q, a_s, at<int32_t>(b.ws, b.L.counts), b.ws, b.L, s);
+  return do_prepare(p, b.x, ti, tw, a_q, a_s, at<int32_t>(b.ws, b.L.counts), b.ws, b.L, s, true, &b.planned);
 }
 
 moe_status fwd_experts(FwdBatch &b, const moe_weights &w, hipStream_t s) {
@@ -484,7 +504,7 @@ moe_status fwd_experts(FwdBatch &b, const moe_weights &w, hipStream_t s) {
   float *a_s = p.act_quant == MOE_QUANT_FP8_TOKEN_GROUP_128 ? at<float>(b.ws, b.L.a_scale) : nullptr;
   const SharedStart sh{&b.p, b.x, b.shared, b.ws, &b.L};
   return do_experts(p, a_q ? a_q : b.x, a_s, w, at<int32_t>(b.ws, b.L.counts), at<void>(b.ws, b.L.fused_out), b.ws,
-                    b.L, s, nullptr, b.shared ? &sh : nullptr, &b.sp);
+                    b.L, s, nullptr, b.shared ? &sh : nullptr, &b.sp, b.planned);
 }
 
 moe_status fwd_finalize(FwdBatch &b, hipStream_t s) {
@@ -654,9 +674,11 @@ moe_status moe_forward(const moe_problem *p, const float *logits, const void *x,
   void *fused = at<void>(workspace, L.fused_out);
   SplitPartials sp;   // set when the down GEMM split K: the combine reads its partial sums
   if (!chunked(*p)) {
-    if ((st = do_prepare(*p, x, ti, tw, a_q, a_s, counts, workspace, L, stream)) != MOE_OK) return st;
+    bool planned = false;
+    if ((st = do_prepare(*p, x, ti, tw, a_q, a_s, counts, workspace, L, stream, true, &planned)) != MOE_OK)
+      return st;
     if ((st = do_experts(*p, a_q ? a_q : x, a_s, *w, counts, fused, workspace, L, stream, events,
-                         shared ? &sh : nullptr, &sp)) != MOE_OK)
+                         shared ? &sh : nullptr, &sp, planned)) != MOE_OK)
       return st;
   } else {
     // Prepare the whole batch's rows, then count, permute and run the experts
@@ -669,11 +691,14 @@ moe_status moe_forward(const moe_problem *p, const float *logits, const void *x,
       moe_problem pc = *p;
       pc.M = std::min(p->chunk_tokens, p->M - m0);
       const int64_t pair0 = m0 * p->topk;
-      if ((st = do_count(pc, ti + pair0, counts, workspace, L, pair0, stream)) != MOE_OK) return st;
+      bool planned = false;
+      if ((st = do_count(pc, ti + pair0, counts, workspace, L, pair0, stream, true, &planned)) != MOE_OK) return st;
       const uint8_t *a = reinterpret_cast<const uint8_t *>(a_q ? a_q : x) + m0 * a_row_bytes;
       const float *as = a_s ? a_s + m0 * (p->K / 128) : nullptr;
       void *fo = reinterpret_cast<uint8_t *>(fused) + pair0 * out_row_bytes;
-      if ((st = do_experts(pc, a, as, *w, counts, fo, workspace, L, stream, events)) != MOE_OK) return st;
+      if ((st = do_experts(pc, a, as, *w, counts, fo, workspace, L, stream, events, nullptr, nullptr, planned)) !=
+          MOE_OK)
+        return st;
     }
   }
   // the permutation prepare just wrote masks dropped / other shards' pairs

@@ -200,8 +200,15 @@ struct DispatchBufs {
   int32_t *status, *counts, *offsets, *chunk_hist, *perm, *inv;
   int64_t perm_len, n_chunks, chunk;
   int clear_status;   // reset the status word first (not for the later chunks of one batch)
+  // the grouped GEMMs' tile plan, written by the counting kernel itself when
+  // count_fused() holds and plan_rows > 0 (rows per tile)
+  int32_t *tiles;
+  int max_tiles;
+  int plan_rows;
 };
 
+// Whether a batch is counted, ranked (and planned) by one single-block kernel.
+bool count_fused(const moe_problem &p);
 hipError_t launch_count_and_permute(const moe_problem &p, const int32_t *ids, int32_t *expert_num_tokens,
                                     const DispatchBufs &b, hipStream_t s);
 // Row quantise / scatter; topk_w non-NULL applies each token's (single)
