@@ -12,58 +12,67 @@
 //
 //  * a workgroup computes a 256-row x 256-column tile (rows: one expert's
 //    slots from the device tile plan; columns: 128 gate + the matching 128 up
-//    weight rows, or 256 output columns), so every operand byte staged in LDS
-//    feeds 256 MFMA columns or rows;
-//  * 8 wavefronts in a 2 x 4 grid, each owning 128 x 64 as 4 x 2 blocks of
-//    v_mfma_f32_32x32x16_bf16 (128 fp32 accumulators per lane, two
-//    wavefronts per SIMD);
-//  * K advances 64 elements per step; both operands go global -> registers ->
-//    a double-buffered, padded LDS tile (72 KB per stage), the next
-//    step's global loads being in flight during the current step's 32 MFMAs
-//    per wavefront; one barrier per step;
+//    weight rows, or 256 output columns) with 8 wavefronts in a 2 x 4 grid,
+//    each owning 128 x 64 as 8 x 4 blocks of v_mfma_f32_16x16x32_bf16 (128
+//    fp32 accumulators per lane, two wavefronts per SIMD);
+//  * the activation rows (A) are copied global -> LDS by the LDS DMA
+//    (global_load_lds_dwordx4: no staging registers, no LDS store
+//    instructions) into 4 stages of 256 rows x 128 bytes (64 elements of K),
+//    the 16-byte chunks of a row XOR-swizzled by the row's low bits so that
+//    the fragment reads of 8 consecutive rows hit distinct banks.  The copy
+//    of K-step s + 3 is issued at the end of step s, into the stage the
+//    step's barrier released, so it has more than two K-steps to land;
+//  * the weights (B) never touch LDS: each wavefront loads its own 16-row
+//    fragments straight from global memory into registers, 1.5 K-steps ahead
+//    through a ring of four sub-step slots.  With the packed weight layout a
+//    wavefront's fragment of one 32-element sub-step is one contiguous 1 KB
+//    (the layout stores exactly this lane order: lane l holds row l % 16, K
+//    elements 16 (l / 16) + 8 p of each 64-element step, p the sub-step), so
+//    every B load is fully coalesced; A fragments are read from LDS in the
+//    same K order.  Against staging both operands through LDS this moves 37%
+//    fewer LDS bytes per flop, and it spreads the global loads over all 8
+//    wavefronts (one wavefront's vector-memory throughput is limited: a probe
+//    of plain 16-byte loads from L2 gave 32 GB/s per CU with 4 wavefronts per
+//    CU, 76 GB/s with 8);
+//  * one barrier per K-step, after an explicit `s_waitcnt vmcnt(16)` (all but
+//    the loads of the last step and a half have landed).  The LDS copies are
+//    issued in inline asm: the compiler cannot tell the four stages apart and
+//    would otherwise wait for every copy in flight before each fragment read,
+//    and a workgroup fence would do the same, so the barrier is a bare one;
 //  * all loads are unconditional (rows past the count read a valid row whose
-//    products are never stored), so the compiler never waits for every
-//    outstanding load in front of the MFMAs; the MFMAs of a wavefront's
-//    32-row blocks past the count are skipped (the main loop is instantiated
-//    per count of live blocks), which on the skewed prefill's 567 row tiles
-//    (10.7% of their rows padding) took the gated GEMM from 3.83 to 3.62 ms
-//    and the down GEMM from 2.21 to 1.96 ms;
+//    products are never stored);
 //  * work items are dealt out XCD by XCD and, inside an XCD's range, grouped
 //    eight row tiles at a time per column tile, so the workgroups resident on
 //    one XCD share both activation rows and weight panels through its L2.
+//
+// Measured on one MI355X on the skewed prefill's expert shapes and tile plan
+// (567 row tiles of 256, packed weights), same box and run, against the
+// previous kernel (both operands staged global -> registers -> LDS, 32x32x16
+// MFMAs): gated GEMM 3.52-3.64 -> 3.06 ms, down GEMM 1.91-1.99 -> 1.72 ms.
+// With both operands made cache-resident the same loop took 3.04 ms: the
+// loads are hidden, and the MFMA pipes are busy about half of the time.
 #include "moe_device.h"
 
 namespace moe {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-// Staging registers are native vectors: HIP's uint4 is a struct whose copies
-// become memcpy, which keeps a staging array in memory (LDS or scratch).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 512;
-constexpr int kRows = 256;            // tile rows (slots)
-constexpr int kCols = 256;            // tile columns (weight rows)
-constexpr int kStep = 128;            // bytes of K per step (64 bf16)
-#ifndef MOE_MFMA_GROUP_M
-#define MOE_MFMA_GROUP_M 8
-#endif
-constexpr int kGroupM = MOE_MFMA_GROUP_M;   // row tiles per L2 group
+constexpr int kRows = 256;              // tile rows (slots)
+constexpr int kCols = 256;              // tile columns (weight rows)
+constexpr int kStep = 128;              // bytes of K per step (64 bf16)
+constexpr int kStages = 4;              // A stages in LDS
+constexpr int kStage = kRows * kStep;   // 32 KB
+constexpr int kGroupM = 8;              // row tiles per L2 group
 
-// LDS tiles are [rows][144 B]: 128 bytes of K plus 16 bytes of padding.  A
-// fragment read is one 16-byte chunk of 16 consecutive rows per 128-bit access
-// pass; with a 144-byte pitch those rows start 36 banks apart, which covers
-// gfx950's 64 banks exactly once.  Unlike an XOR swizzle, the padding keeps
-// every K sub-step at a constant offset from the row's address, so a fragment
-// needs one address register per row block instead of one per sub-step.
-constexpr int kPitch = kStep + 16;
-__device__ __forceinline__ int lds_at(int row, int b) { return row * kPitch + b; }
+#define MOE_LP(p) ((__attribute__((address_space(3))) void *)(p))
 
 template <bool GATED, bool PACKED>
-__global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const GemmParams g, int n_tiles) {
-  __shared__ __attribute__((aligned(16))) uint8_t As[2][kRows * kPitch];
-  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][kCols * kPitch];
+__global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(const GemmParams g, int n_tiles) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStage];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = wv >> 2, wn = wv & 3;
@@ -94,174 +103,168 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const GemmParams g,
     row0 = (int64_t)d[1] + d[2];
     T = d[3];
   }
-
   const int64_t row_bytes = g.Kred * 2;
   const int nk = (int)(row_bytes / kStep);
-  const int chunk = tid & 7;
   const PackedGeom pg = packed_geom(g.Nw, row_bytes, GATED);
   const int64_t kstride = PACKED ? packed_kstep_stride(pg) : kStep;
 
-  // This thread stages chunk `chunk` of rows (tid / 8) + 64 i, i < 4, of both
-  // operand tiles.  Rows past the tile's count and padding slots read row 0
-  // instead: an A row only feeds its own output row, and the epilogue writes
-  // nothing for those rows, so their contents never matter (and no select on
-  // loaded data forces an early wait for the loads).
+  // A copies: wavefront wv fills rows wv*32 + 8j + lane/8 (j < 4) of each
+  // stage; lane l writes slot l % 8 of its row, which holds global chunk
+  // (l % 8) ^ (row & 7) = (l % 8) ^ (l / 8).  Rows past the tile's count and
+  // padding slots read row 0 instead: an A row only feeds its own output row,
+  // and the epilogue writes nothing for those.
+  const int rr = lane >> 3, cg = (lane & 7) ^ rr;
   const uint8_t *a_src[4];
-  // Weight rows: base_i + (tid / 8) with base_i a multiple of 64, so in both
-  // layouts the address splits into a per-lane part (row within the 64-row
-  // group, chunk) shared by all four rows and a wavefront-uniform part per row
-  // group, which stays in scalar registers.
-  int64_t b_uni[4];
-  auto wbase = [&](int i) -> int64_t {
-    if (GATED) return i < 2 ? (int64_t)nt * 128 + 64 * i : g.half_n + (int64_t)nt * 128 + 64 * (i - 2);
-    return (int64_t)nt * kCols + 64 * i;
-  };
-  const int r0 = tid >> 3;
-  int64_t b_lane;
-  if (PACKED)
-    b_lane = packed_piece(pg, e, wbase(0) + r0, 0, chunk) - packed_piece(pg, e, wbase(0), 0, 0);
-  else
-    b_lane = (int64_t)r0 * row_bytes + chunk * 16;
-  const uint8_t *b_src = reinterpret_cast<const uint8_t *>(g.w) + b_lane;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    b_uni[i] = PACKED ? packed_piece(pg, e, wbase(i), 0, 0) : ((int64_t)e * g.Nw + wbase(i)) * row_bytes;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (tid >> 3) + 64 * i;
-    a_src[i] = reinterpret_cast<const uint8_t *>(g.a) + chunk * 16;
-    if (r < T) {
-      const int64_t s = row0 + r;
+  for (int j = 0; j < 4; ++j) {
+    const int q = wv * 32 + 8 * j + rr;
+    a_src[j] = reinterpret_cast<const uint8_t *>(g.a) + cg * 16;
+    if (q < T) {
+      const int64_t s = row0 + q;
       int64_t arow = s;
       if (g.perm) {
         const int f = g.perm[s];
         arow = (f >= 0 && f < g.n_pairs) ? f / g.topk : -1;
       }
-      if (arow >= 0) a_src[i] = reinterpret_cast<const uint8_t *>(g.a) + arow * row_bytes + chunk * 16;
+      if (arow >= 0) a_src[j] = reinterpret_cast<const uint8_t *>(g.a) + arow * row_bytes + cg * 16;
     }
   }
+  // B: this wavefront's four 16-row blocks -- gated: gate, gate, up, up (act
+  // columns wn*32 + 16 (nb % 2)); down: four adjacent blocks of outputs.
+  auto brow = [&](int nb) -> int64_t {
+    if (GATED) return (nb < 2 ? (int64_t)0 : g.half_n) + (int64_t)nt * 128 + wn * 32 + (nb & 1) * 16;
+    return (int64_t)nt * kCols + wn * 64 + nb * 16;
+  };
+  const int bc = 2 * (lane >> 4);   // lane's first 16-byte chunk of a K-step
+  // a small per-lane offset, plus wavefront-uniform block and step offsets
+  const uint32_t b_lane = PACKED ? (uint32_t)(packed_piece(pg, e, brow(0) + (lane & 15), 0, bc) -
+                                              packed_piece(pg, e, brow(0), 0, 0))
+                                 : (uint32_t)((lane & 15) * row_bytes + bc * 16);
+  int64_t b_off[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+    b_off[nb] = PACKED ? packed_piece(pg, e, brow(nb), 0, 0) : ((int64_t)e * g.Nw + brow(nb)) * row_bytes;
+  const uint8_t *const wb = reinterpret_cast<const uint8_t *>(g.w);
+  constexpr int64_t kPstep = PACKED ? 1024 : 16;   // the second sub-step of a K-step
 
-  f32x16 acc[4][2];
+  f32x4 acc[8][4];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.0f;
+    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  bf16x8 bf[4][4];   // [slot][nb]: B of four consecutive 32-element sub-steps
 
-  // Two register sets of staged operands: step j's loads land in set j % 2,
-  // issued two steps before they are stored to LDS.
-  u32x4 ra[2][4], rb[2][4];
-  auto gload = [&](int set, int ks) {
+  // LDS byte address of this wavefront's first copy row in stage 0
+  const uint32_t lds0 = (uint32_t)(uintptr_t)MOE_LP(smem) + (uint32_t)(wv * 32) * kStep;
+  // A of K-step ks into `stage`.  Issued in asm: the compiler's wait counting
+  // cannot tell the stages apart and would wait for every copy in flight
+  // before each fragment read; the copies' own waits are the explicit vmcnt
+  // before each barrier.
+  auto copy_a = [&](int stage, int ks) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[set][i] = *reinterpret_cast<const u32x4 *>(a_src[i] + (int64_t)ks * kStep);
-      rb[set][i] = *reinterpret_cast<const u32x4 *>(b_src + b_uni[i] + (int64_t)ks * kstride);
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(stage * kStage + 8 * j * kStep));
+      const uint8_t *src = a_src[j] + (int64_t)ks * kStep;
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_nop 0"
+                   :: "s"(m0v), "v"(src) : "memory", "m0");
     }
   };
-  auto lstore = [&](int st, int set) {
+  // B of sub-step t (K-step t / 2, sub-step t % 2) into `slot`
+  auto load_b = [&](int slot, int t) {
+    const int ks = min(t >> 1, nk - 1), p = t & 1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (tid >> 3) + 64 * i;
-      *reinterpret_cast<u32x4 *>(&As[st][lds_at(r, chunk * 16)]) = ra[set][i];
-      *reinterpret_cast<u32x4 *>(&Bs[st][lds_at(r, chunk * 16)]) = rb[set][i];
-    }
+    for (int nb = 0; nb < 4; ++nb)
+      bf[slot][nb] = *reinterpret_cast<const bf16x8 *>(wb + (b_off[nb] + (int64_t)ks * kstride + p * kPstep) + b_lane);
   };
-  // B rows of this wavefront's two column blocks: gate and up (gated), or two
-  // adjacent 32-column blocks (down).
-  const int brow0 = GATED ? wn * 32 : wn * 64;
-  const int brow1 = GATED ? 128 + wn * 32 : wn * 64 + 32;
-  // One K-step of MFMAs from LDS stage st over this wavefront's first NMB
-  // 32-row blocks (the blocks past the tile's row count are skipped: their
-  // rows are never stored).  The step's global loads for K-step ks go out
-  // spread over the MFMAs, two per 16-element sub-step, into register set
-  // `set`: issued back to back, a workgroup's loads fill the texture address
-  // queue and every wavefront stalls at issue until it drains, with its MFMAs
-  // queued behind the loads.
-  auto compute = [&](auto NMB_, int st, int set, int ks) {
-    constexpr int NMB = decltype(NMB_)::value;
-    const uint8_t *A = As[st];
-    const uint8_t *B = Bs[st];
+  // one 32-element sub-step p from A `stage` and B `slot`
+  auto substep = [&](int stage, int slot, int p) {
+    const uint8_t *As = smem + stage * kStage;
+    const int c = bc + p;
+    bf16x8 af[8];
 #pragma unroll
-    for (int kk = 0; kk < kStep / 32; ++kk) {
-      const int boff = kk * 32 + (lane >> 5) * 16;
-      bf16x8 b0, b1;
-      if (NMB > 0) {
-        b0 = *reinterpret_cast<const bf16x8 *>(B + lds_at(brow0 + (lane & 31), boff));
-        b1 = *reinterpret_cast<const bf16x8 *>(B + lds_at(brow1 + (lane & 31), boff));
-      }
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        if (mb < NMB) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(A + lds_at(wm * 128 + mb * 32 + (lane & 31), boff));
-          acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc[mb][0], 0, 0, 0);
-          acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc[mb][1], 0, 0, 0);
-        }
-        if (mb == 1) {
-          ra[set][kk] = *reinterpret_cast<const u32x4 *>(a_src[kk] + (int64_t)ks * kStep);
-          rb[set][kk] = *reinterpret_cast<const u32x4 *>(b_src + b_uni[kk] + (int64_t)ks * kstride);
-        }
-      }
-      // keep each sub-step's two loads with its MFMAs
-      __builtin_amdgcn_sched_barrier(0);
+    for (int mb = 0; mb < 8; ++mb) {
+      const int r = wm * 128 + mb * 16 + (lane & 15);
+      af[mb] = *reinterpret_cast<const bf16x8 *>(As + r * kStep + ((c ^ (r & 7)) << 4));
     }
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb], bf[slot][nb], acc[mb][nb], 0, 0, 0);
   };
 
-  // Pipeline: LDS stage s % 2 holds K-step s while it is multiplied; register
-  // set s % 2 receives step s + 2 during that multiply (its step s was stored
-  // to LDS before the barrier that opened it), and step s + 1, loaded during
-  // the previous multiply, is stored to the other stage after it.  Every load
-  // thus has about two steps of matrix work to arrive in, and steps past the
-  // last reload the last one instead of branching around the loads.  nk is
-  // even (the host requires K and I to be multiples of 128 elements), so the
-  // loop runs in pairs and every register-set index is a constant.  The loop
-  // is instantiated per count of this wavefront's 32-row blocks that hold
-  // real rows (a tile's last rows of an expert are often fewer than 256).
-  auto main_loop = [&](auto NMB) {
-    gload(0, 0);
-    lstore(0, 0);
-    gload(1, min(1, nk - 1));
-    __syncthreads();
-    for (int ks = 0; ks < nk; ks += 2) {
-      compute(NMB, 0, 0, min(ks + 2, nk - 1));
-      lstore(1, 1);
-      __syncthreads();
-      compute(NMB, 1, 1, min(ks + 3, nk - 1));
-      lstore(0, 0);
-      __syncthreads();
-    }
+  // Prologue: A steps 0-2 copying, B sub-steps 0-2.  The order matters:
+  // vmcnt counts loads in issue order.
+  copy_a(0, 0);
+  copy_a(1, min(1, nk - 1));
+  load_b(0, 0);
+  load_b(1, 1);
+  load_b(2, 2);
+  copy_a(2, min(2, nk - 1));
+  // K-step ks (A stage ks % 4, B slots 2ks % 4 and (2ks + 1) % 4, all
+  // compile-time): each sub-step t first issues the B loads of sub-step t + 3
+  // into the slot sub-step t - 1 freed; the A copy of ks + 3 goes out at the
+  // end, into the stage the barrier released.  Steps past the last re-copy
+  // and reload the last one instead of branching around the loads.
+  auto kstep = [&](auto ST_, int ks) {
+    constexpr int ST = decltype(ST_)::value, S0 = (2 * ST) & 3, S1 = (2 * ST + 1) & 3;
+    // vmcnt(16): all but the last 16 loads (the previous step's B loads and
+    // A copy, and the A copy before them) have landed, among them the A copy
+    // of ks and the B of this step's first sub-step; after the barrier
+    // everyone's A of ks is in and the stage of ks - 1 is free.
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    load_b((S0 + 3) & 3, 2 * ks + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    substep(ST, S0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_b((S1 + 3) & 3, 2 * ks + 4);
+    __builtin_amdgcn_sched_barrier(0);
+    substep(ST, S1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    copy_a((ST + 3) & 3, min(ks + 3, nk - 1));
   };
-  const int nmb = min(4, max(0, (T - wm * 128 + 31) / 32));
-  switch (nmb) {
-    case 4: main_loop(std::integral_constant<int, 4>{}); break;
-    case 3: main_loop(std::integral_constant<int, 3>{}); break;
-    case 2: main_loop(std::integral_constant<int, 2>{}); break;
-    case 1: main_loop(std::integral_constant<int, 1>{}); break;
-    default: main_loop(std::integral_constant<int, 0>{}); break;
+  // nk is even (K and I are multiples of 128 elements): groups of four steps,
+  // then a last pair when nk % 4 == 2
+  int ks = 0;
+  for (; ks + 4 <= nk; ks += 4) {
+    kstep(std::integral_constant<int, 0>{}, ks);
+    kstep(std::integral_constant<int, 1>{}, ks + 1);
+    kstep(std::integral_constant<int, 2>{}, ks + 2);
+    kstep(std::integral_constant<int, 3>{}, ks + 3);
+  }
+  if (ks < nk) {
+    kstep(std::integral_constant<int, 0>{}, ks);
+    kstep(std::integral_constant<int, 1>{}, ks + 1);
   }
 
-  // Epilogue.  Accumulator element i of a 32x32 block sits at column
-  // (lane % 32) and row 8 (i / 4) + 4 (lane / 32) + i % 4.  The bf16 tile is
-  // staged in LDS (rows 0-127 in the A buffers, 128-255 in the B buffers) and
-  // leaves as whole rows of 16-byte stores; the 16-byte row padding puts the
-  // two rows of each 2-byte store instruction on different banks.
+  // Epilogue.  A 16x16 accumulator block holds column l % 16 and rows
+  // 4 (l / 16) + i in lane l.  The bf16 tile is staged in the (now idle) A
+  // stages, rows of kRowB bytes with their 16-byte chunks XOR-swizzled by row,
+  // and leaves as whole rows of 16-byte stores.
   constexpr int kOutCols = GATED ? 128 : kCols;
-  constexpr int kRowB = kOutCols * 2, kSP = kRowB + 16, kChunk = kRowB / 16;
-  static_assert(128 * kSP <= 2 * kRows * kPitch, "half a tile fits each operand's LDS buffers");
-  __syncthreads();   // every wavefront is done reading the operand tiles
-  uint8_t *half = wm == 0 ? &As[0][0] : &Bs[0][0];   // rows wm*128 .. +128
+  constexpr int kRowB = kOutCols * 2, kChunk = kRowB / 16;
+  static_assert(kRows * kRowB <= kStages * kStage, "the output tile fits the A stages");
+  auto osw = [&](int r, int byte) { return r * kRowB + ((((byte >> 4) ^ (r & 7)) << 4) | (byte & 15)); };
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0): the last (unused) copies have landed
+  __syncthreads();
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
+  for (int mb = 0; mb < 8; ++mb) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      uint8_t *row = half + (mb * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3)) * kSP;
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm * 128 + mb * 16 + (lane >> 4) * 4 + i;
       if constexpr (GATED) {
-        const float v = gated_act(acc[mb][0][i], acc[mb][1][i], g.act);
-        *reinterpret_cast<uint16_t *>(row + (wn * 32 + (lane & 31)) * 2) = f32_to_bf16_bits(v);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const float v = gated_act(acc[mb][nb][i], acc[mb][nb + 2][i], g.act);
+          *reinterpret_cast<uint16_t *>(smem + osw(r, (wn * 32 + nb * 16 + (lane & 15)) * 2)) = f32_to_bf16_bits(v);
+        }
       } else {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          *reinterpret_cast<uint16_t *>(row + (wn * 64 + nb * 32 + (lane & 31)) * 2) = f32_to_bf16_bits(acc[mb][nb][i]);
+        for (int nb = 0; nb < 4; ++nb)
+          *reinterpret_cast<uint16_t *>(smem + osw(r, (wn * 64 + nb * 16 + (lane & 15)) * 2)) =
+              f32_to_bf16_bits(acc[mb][nb][i]);
       }
     }
   }
@@ -277,9 +280,8 @@ __global__ __launch_bounds__(kThreads) void mfma_gemm_kernel(const GemmParams g,
         if (orow < 0 || orow >= g.n_pairs) continue;
       }
     }
-    const uint8_t *src = (r < 128 ? &As[0][0] : &Bs[0][0]) + (r & 127) * kSP + off;
     *reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(g.out) + (orow * g.ldo + col0) * 2 + off) =
-        *reinterpret_cast<const u32x4 *>(src);
+        *reinterpret_cast<const u32x4 *>(smem + osw(r, off));
   }
 }
 
@@ -289,9 +291,8 @@ int mfma_gemm_tile_rows() { return kRows; }
 
 bool mfma_gemm_fits(int w_dtype, int act_dtype, int64_t K, int64_t I) {
   // bf16 in and out; gated column tiles of 128 act columns, down column tiles
-  // of 256 outputs, K-steps of 64 elements on both reductions.
-  return w_dtype == MOE_DTYPE_BF16 && act_dtype == MOE_DTYPE_BF16 && I % 128 == 0 && K % 256 == 0 &&
-         I % 64 == 0;
+  // of 256 outputs, an even number of 64-element K-steps on both reductions.
+  return w_dtype == MOE_DTYPE_BF16 && act_dtype == MOE_DTYPE_BF16 && I % 128 == 0 && K % 256 == 0;
 }
 
 int mfma_gemm_n_tiles(GemmKind kind, int64_t Nw) { return (int)(kind == kGemmGatedAct ? Nw / 256 : Nw / kCols); }
