@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ y, c
       uint32_t u[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        u[i] = (uint32_t)f32_to_bf16_bits(acc[2 * i]) | ((uint32_t)f32_to_bf16_bits(acc[2 * i + 1]) << 16);
+        u[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
       *reinterpret_cast<uint4 *>(out + (int64_t)m * K + c) = make_uint4(u[0], u[1], u[2], u[3]);
     } else {
       float4 *dst = reinterpret_cast<float4 *>(out + (int64_t)m * K + c);
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(256) void combine_split_kernel(const float *__restr
     uint32_t o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      o[i] = (uint32_t)f32_to_bf16_bits(acc[2 * i]) | ((uint32_t)f32_to_bf16_bits(acc[2 * i + 1]) << 16);
+      o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
     *reinterpret_cast<uint4 *>(out + (int64_t)m * K + c) = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }

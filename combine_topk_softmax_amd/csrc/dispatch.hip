@@ -231,7 +231,7 @@ __global__ __launch_bounds__(256) void dispatch_rows_kernel(const TIn *__restric
           uint32_t u[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            u[i] = (uint32_t)f32_to_bf16_bits(v[2 * i]) | ((uint32_t)f32_to_bf16_bits(v[2 * i + 1]) << 16);
+            u[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
           *reinterpret_cast<uint4 *>(reinterpret_cast<TIn *>(a_out) + d * K + c0) = make_uint4(u[0], u[1], u[2], u[3]);
         } else {
           float4 *dst = reinterpret_cast<float4 *>(reinterpret_cast<TIn *>(a_out) + d * K + c0);

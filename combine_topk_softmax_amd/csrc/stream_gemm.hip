@@ -139,6 +139,7 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
 
   __shared__ __attribute__((aligned(16))) uint8_t As[2][TMAX * 128];
   __shared__ __attribute__((aligned(16))) float Sa[2][TMAX];
+  __shared__ int32_t Orow[GATED ? 1 : TMAX];   // down: output row of each tile row
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int total = *g.t.tile_count * n_tiles;
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
   // the 16 lanes holding a row's columns in a wavefront, then across the
   // wavefronts of the group through LDS; the codes are staged in LDS and
   // written as whole rows.
-  auto quant_epilogue = [&]<int NMB>(f32x4 (&acc)[NMB][NBW]) {
+  auto quant_epilogue = [&]<int NMB, int ACT>(f32x4 (&acc)[NMB][NBW]) {
     constexpr int kGroupWaves = 8 / GB;   // wavefronts whose columns form one group
     constexpr int kRowCodes = 128 * GB;   // code bytes per row of the item
     static_assert(NMB * 16 * kRowCodes <= 2 * TMAX * 128, "the codes fit the A buffers");
@@ -248,7 +249,7 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
         float m = 0.0f;
 #pragma unroll
         for (int gb = 0; gb < GB; ++gb) {
-          v[mb][gb][i] = gated_act(acc[mb][gb][i], acc[mb][gb + GB][i], g.act);
+          v[mb][gb][i] = gated_act<ACT>(acc[mb][gb][i], acc[mb][gb + GB][i]);
           m = fmaxf(m, fabsf(v[mb][gb][i]));
         }
 #pragma unroll
@@ -403,12 +404,30 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
       }
     };
 
+    // Down: the output row of tile row tid (slot order, or through out_perm;
+    // padding slots and rows past the count give -1), loaded first so that no
+    // later wait stops on it.
+    int orow_t = -1;
+    if constexpr (!GATED) {
+      if (tid < T) {
+        orow_t = (int)(row0 + tid);   // slots are int32 in the tile plan
+        if (out_perm) {
+          orow_t = out_perm[orow_t];
+          if (orow_t >= g.n_pairs) orow_t = -1;
+        }
+      }
+    }
+
     // Pipeline: A two K-steps ahead (registers -> LDS), weights D ahead.
     loadA(0, 0);
     loadA(1, min(1, nk - 1));
 #pragma unroll
     for (int j = 0; j < D; ++j) loadW(j, min(j, nk - 1));
     storeA(0, 0);
+    if constexpr (!GATED) {
+      // the first barrier publishes the output rows read before the loads
+      if (tid < NMB * 16) Orow[tid] = orow_t;
+    }
     __syncthreads();
     for (int kb = 0; kb < nk; kb += U) {
 #pragma unroll
@@ -422,99 +441,107 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
       }
     }
 
-    // Epilogue: in a 16x16 block, lane holds column r16 of rows 4*q + i.
-    if constexpr (GATED && kScaled) {
-      if (g.out_scale) {
-        quant_epilogue.template operator()<NMB>(acc);
+    // Epilogue: in a 16x16 block, lane holds column r16 of rows 4*q + i.  The
+    // activation is resolved once per item, outside the per-element code.
+    auto epilogue = [&]<int ACT>() {
+      if constexpr (GATED && kScaled) {
+        if (g.out_scale) {
+          quant_epilogue.template operator()<NMB, ACT>(acc);
+          return;
+        }
+      }
+      if constexpr (OUT_BF16) {
+        // bf16 tiles go through LDS and leave as whole rows of 16-byte stores
+        // (one 2-byte store per element cost a fifth of the down GEMM on the
+        // DeepSeek shapes).  Rows are staged in passes that fit the A buffers;
+        // the 16-byte row padding spreads the 4 rows a store instruction
+        // touches over different banks.
+        constexpr int kCols = GATED ? 128 * GB : 128 * NBW;
+        constexpr int kRowBytes = kCols * 2;
+        constexpr int kPitch = kRowBytes + 16;
+        constexpr int kFit = (2 * TMAX * 128 / kPitch) / 16 * 16;
+        constexpr int RP = kFit < NMB * 16 ? kFit : NMB * 16;
+        constexpr int kChunks = kRowBytes / 16;
+        static_assert(RP >= 16, "staging buffer holds at least one row block");
+        uint8_t *stage = &As[0][0];
+        const int64_t col0 = (int64_t)nt * kCols;
+        __syncthreads();   // every wavefront is done reading the A tiles
+#pragma unroll
+        for (int p0 = 0; p0 < NMB * 16; p0 += RP) {
+#pragma unroll
+          for (int mb = p0 / 16; mb < (p0 + RP) / 16 && mb < NMB; ++mb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              uint8_t *row = stage + (mb * 16 + q * 4 + i - p0) * kPitch;
+              if constexpr (GATED) {
+#pragma unroll
+                for (int gb = 0; gb < GB; ++gb) {
+                  const float v = gated_act<ACT>(acc[mb][gb][i], acc[mb][gb + GB][i]);
+                  *reinterpret_cast<uint16_t *>(row + (wv * 16 * GB + gb * 16 + r16) * 2) = f32_to_bf16_bits(v);
+                }
+              } else {
+#pragma unroll
+                for (int b = 0; b < NBW; ++b)
+                  *reinterpret_cast<uint16_t *>(row + (wv * 16 * NBW + b * 16 + r16) * 2) =
+                      f32_to_bf16_bits(acc[mb][b][i]);
+              }
+            }
+          }
+          __syncthreads();
+          const int nrows = min(RP, T - p0);
+          for (int c = tid; c < nrows * kChunks; c += kThreads) {
+            const int rl = c / kChunks, off = (c - rl * kChunks) * 16;
+            int64_t orow = row0 + p0 + rl;
+            if constexpr (!GATED) {
+              orow = Orow[p0 + rl];
+              if (orow < 0) continue;
+            }
+            *reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(out) + (orow * g.ldo + col0) * 2 + off) =
+                *reinterpret_cast<const u32x4 *>(stage + rl * kPitch + off);
+          }
+          __syncthreads();
+        }
         return;
       }
-    }
-    if constexpr (OUT_BF16) {
-      // bf16 tiles go through LDS and leave as whole rows of 16-byte stores
-      // (one 2-byte store per element cost a fifth of the down GEMM on the
-      // DeepSeek shapes).  Rows are staged in passes that fit the A buffers;
-      // the 16-byte row padding spreads the 4 rows a store instruction
-      // touches over different banks.
-      constexpr int kCols = GATED ? 128 * GB : 128 * NBW;
-      constexpr int kRowBytes = kCols * 2;
-      constexpr int kPitch = kRowBytes + 16;
-      constexpr int kFit = (2 * TMAX * 128 / kPitch) / 16 * 16;
-      constexpr int RP = kFit < NMB * 16 ? kFit : NMB * 16;
-      constexpr int kChunks = kRowBytes / 16;
-      static_assert(RP >= 16, "staging buffer holds at least one row block");
-      uint8_t *stage = &As[0][0];
-      const int64_t col0 = (int64_t)nt * kCols;
-      __syncthreads();   // every wavefront is done reading the A tiles
 #pragma unroll
-      for (int p0 = 0; p0 < NMB * 16; p0 += RP) {
+      for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
-        for (int mb = p0 / 16; mb < (p0 + RP) / 16 && mb < NMB; ++mb) {
+        for (int i = 0; i < 4; ++i) {
+          const int r = mb * 16 + q * 4 + i;
+          if (r >= T) continue;
+          const int64_t slot = row0 + r;
+          if constexpr (GATED) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            uint8_t *row = stage + (mb * 16 + q * 4 + i - p0) * kPitch;
-            if constexpr (GATED) {
+            for (int gb = 0; gb < GB; ++gb) {
+              const float v = gated_act<ACT>(acc[mb][gb][i], acc[mb][gb + GB][i]);
+              const int64_t col = (int64_t)nt * 128 * GB + wv * 16 * GB + gb * 16 + r16;
+              if constexpr (OUT_BF16)
+                reinterpret_cast<uint16_t *>(out)[slot * g.ldo + col] = f32_to_bf16_bits(v);
+              else
+                reinterpret_cast<float *>(out)[slot * g.ldo + col] = v;
+            }
+          } else {
+            const int64_t orow = Orow[r];
+            if (orow < 0) continue;
 #pragma unroll
-              for (int gb = 0; gb < GB; ++gb) {
-                const float v = gated_act(acc[mb][gb][i], acc[mb][gb + GB][i], g.act);
-                *reinterpret_cast<uint16_t *>(row + (wv * 16 * GB + gb * 16 + r16) * 2) = f32_to_bf16_bits(v);
-              }
-            } else {
-#pragma unroll
-              for (int b = 0; b < NBW; ++b)
-                *reinterpret_cast<uint16_t *>(row + (wv * 16 * NBW + b * 16 + r16) * 2) =
-                    f32_to_bf16_bits(acc[mb][b][i]);
+            for (int b = 0; b < NBW; ++b) {
+              const int64_t col = (int64_t)nt * (128 * NBW) + wv * (16 * NBW) + b * 16 + r16;
+              if constexpr (OUT_BF16)
+                reinterpret_cast<uint16_t *>(out)[orow * g.ldo + col] = f32_to_bf16_bits(acc[mb][b][i]);
+              else
+                reinterpret_cast<float *>(out)[orow * g.ldo + col] = acc[mb][b][i];
             }
           }
         }
-        __syncthreads();
-        const int nrows = min(RP, T - p0);
-        for (int c = tid; c < nrows * kChunks; c += kThreads) {
-          const int rl = c / kChunks, off = (c - rl * kChunks) * 16;
-          const int64_t slot = row0 + p0 + rl;
-          int64_t orow = slot;
-          if constexpr (!GATED) {
-            if (out_perm) {
-              orow = out_perm[slot];
-              if (orow < 0 || orow >= g.n_pairs) continue;
-            }
-          }
-          *reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(out) + (orow * g.ldo + col0) * 2 + off) =
-              *reinterpret_cast<const u32x4 *>(stage + rl * kPitch + off);
-        }
-        __syncthreads();
       }
-      return;
-    }
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = mb * 16 + q * 4 + i;
-        if (r >= T) continue;
-        const int64_t slot = row0 + r;
-        if constexpr (GATED) {
-#pragma unroll
-          for (int gb = 0; gb < GB; ++gb) {
-            const float v = gated_act(acc[mb][gb][i], acc[mb][gb + GB][i], g.act);
-            const int64_t col = (int64_t)nt * 128 * GB + wv * 16 * GB + gb * 16 + r16;
-            if constexpr (OUT_BF16)
-              reinterpret_cast<uint16_t *>(out)[slot * g.ldo + col] = f32_to_bf16_bits(v);
-            else
-              reinterpret_cast<float *>(out)[slot * g.ldo + col] = v;
-          }
-        } else {
-          const int64_t orow = out_perm ? out_perm[slot] : slot;
-          if (orow < 0 || (out_perm && orow >= g.n_pairs)) continue;
-#pragma unroll
-          for (int b = 0; b < NBW; ++b) {
-            const int64_t col = (int64_t)nt * (128 * NBW) + wv * (16 * NBW) + b * 16 + r16;
-            if constexpr (OUT_BF16)
-              reinterpret_cast<uint16_t *>(out)[orow * g.ldo + col] = f32_to_bf16_bits(acc[mb][b][i]);
-            else
-              reinterpret_cast<float *>(out)[orow * g.ldo + col] = acc[mb][b][i];
-          }
-        }
-      }
+    };
+    if constexpr (GATED) {
+      if (g.act == MOE_ACTIVATION_GELU)
+        epilogue.template operator()<MOE_ACTIVATION_GELU>();
+      else
+        epilogue.template operator()<MOE_ACTIVATION_SILU>();
+    } else {
+      epilogue.template operator()<MOE_ACTIVATION_SILU>();
     }
   };
 
@@ -586,7 +613,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
       uint32_t u[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        u[i] = (uint32_t)f32_to_bf16_bits(acc[2 * i]) | ((uint32_t)f32_to_bf16_bits(acc[2 * i + 1]) << 16);
+        u[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
       *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out) + (int64_t)pair * K + c) =
           make_uint4(u[0], u[1], u[2], u[3]);
     } else {
