@@ -208,8 +208,7 @@ __global__ __launch_bounds__(256) void dispatch_rows_kernel(const TIn *__restric
       float amax = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+      amax = row16_max(amax);
       const float sc = group_scale(amax);
       uint32_t lo = 0, hi = 0;
 #pragma unroll
@@ -271,8 +270,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const float *__restrict
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+    amax = row16_max(amax);
     const float sc = group_scale(amax);
     uint32_t lo = 0, hi = 0;
 #pragma unroll

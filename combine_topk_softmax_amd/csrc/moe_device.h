@@ -52,6 +52,26 @@ __device__ __forceinline__ uint32_t quant_e4m3(float x, float scale) {
   return f32_to_e4m3(t);
 }
 
+// The same with the reciprocal of the scale (the second-stage quantisation
+// of act in GEMM epilogues): x * inv is within 2 ulp of x / scale, which can
+// move a code only for values that close to an e4m3 rounding boundary.
+__device__ __forceinline__ uint32_t quant_e4m3_inv(float x, float inv) {
+  float t = x * inv;
+  t = fminf(fmaxf(t, -448.0f), 448.0f);
+  return f32_to_e4m3(t);
+}
+
+// Maximum over the 16 lanes of a DPP row (lanes 16r .. 16r + 15), returned in
+// every lane: rotations by 8, 4, 2 and 1 within the row, each combined with
+// fmaxf, with no LDS traffic.
+__device__ __forceinline__ float row16_max(float m) {
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x128, 0xf, 0xf, false)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x124, 0xf, 0xf, false)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x122, 0xf, 0xf, false)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x121, 0xf, 0xf, false)));
+  return m;
+}
+
 // ------------------------------------------------------------ activation
 
 // act(gate) * up of the gated GEMM epilogues: silu_and_mul, or gelu_and_mul

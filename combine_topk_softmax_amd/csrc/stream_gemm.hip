@@ -252,24 +252,28 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
           v[mb][gb][i] = gated_act<ACT>(acc[mb][gb][i], acc[mb][gb + GB][i]);
           m = fmaxf(m, fabsf(v[mb][gb][i]));
         }
-#pragma unroll
-        for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
+        m = row16_max(m);
         if (r16 == 0) rmax[(mb * 16 + q * 4 + i) * 8 + wv] = m;
       }
     }
     __syncthreads();
-    float sc[NMB][4];
+    float inv[NMB][4];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = mb * 16 + q * 4 + i;
+        // the group's per-wavefront maxima are contiguous: 16-byte reads
         float amax = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kGroupWaves; ++w) amax = fmaxf(amax, rmax[r * 8 + grp * kGroupWaves + w]);
-        sc[mb][i] = group_scale(amax);
+        for (int w = 0; w < kGroupWaves; w += 4) {
+          const float4 m4 = *reinterpret_cast<const float4 *>(&rmax[r * 8 + grp * kGroupWaves + w]);
+          amax = fmaxf(amax, fmaxf(fmaxf(m4.x, m4.y), fmaxf(m4.z, m4.w)));
+        }
+        const float sc = group_scale(amax);
+        inv[mb][i] = 1.0f / sc;
         if (wv % kGroupWaves == 0 && r16 == 0 && r < T)
-          g.out_scale[(row0 + r) * (g.ldo / 128) + (int64_t)nt * GB + grp] = sc[mb][i];
+          g.out_scale[(row0 + r) * (g.ldo / 128) + (int64_t)nt * GB + grp] = sc;
       }
     }
     __syncthreads();   // the row maxima are read: their space takes the codes
@@ -280,7 +284,7 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
 #pragma unroll
         for (int gb = 0; gb < GB; ++gb)
           codes[(mb * 16 + q * 4 + i) * kRowCodes + wv * 16 * GB + gb * 16 + r16] =
-              (uint8_t)quant_e4m3(v[mb][gb][i], sc[mb][i]);
+              (uint8_t)quant_e4m3_inv(v[mb][gb][i], inv[mb][i]);
     __syncthreads();
     // kRowCodes / 16 threads per row, 16 bytes each
     constexpr int kChunksRow = kRowCodes / 16;
