@@ -123,11 +123,17 @@ def cpu_baseline(wl, d, sample_tokens: int):
     host = {k: (v.cpu() if hasattr(v, "cpu") else v) for k, v in d.items()}
     n = sample_tokens
     if n <= 0:
-        # size the sample to roughly 15 s of oracle work from a one-token probe
+        # size the sample to roughly 15 s of oracle work: probes of 1 and 9
+        # tokens split the call's fixed cost (the router over all tokens) from
+        # the cost per sampled token
         t0 = time.perf_counter()
         oracle.moe_tokens(wl, host, [0])
-        one = max(time.perf_counter() - t0, 1e-3)
-        n = int(max(1, min(wl.M, 15.0 / one)))
+        t1 = time.perf_counter()
+        oracle.moe_tokens(wl, host, list(range(min(9, wl.M))))
+        t9 = time.perf_counter() - t1
+        per = max((t9 - (t1 - t0)) / max(min(9, wl.M) - 1, 1), 1e-4)
+        fixed = max((t1 - t0) - per, 0.0)
+        n = int(max(1, min(wl.M, (15.0 - fixed) / per)))
     toks = pick(wl.M, n, seed=7)
     t0 = time.perf_counter()
     oracle.moe_tokens(wl, host, toks)
