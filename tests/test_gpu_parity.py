@@ -134,6 +134,62 @@ def test_prepare_batched_parity(name):
         np.testing.assert_array_equal(a_cpu.float().numpy()[rows], x.float().numpy()[toks])
 
 
+def _e4m3_rounding_edges() -> np.ndarray:
+    """Every positive e4m3 value (codes 1..0x7e) and every midpoint between
+    consecutive ones: the normal midpoints have 4 significant bits and the
+    subnormal ones are odd multiples of 2^-10, so all are exact in bf16."""
+    vals = oracle.e4m3_decode(np.arange(1, 0x7F, dtype=np.uint8))
+    mids = (vals[:-1] + vals[1:]) / 2
+    return np.concatenate([vals, mids, [vals[0] / 2]])
+
+
+def test_fp8_quantiser_rounding_edges():
+    """The token-group-128 quantiser at its rounding edges, bit for bit against
+    the oracle: groups whose scale is exactly 1 or 2^-3 (amax 448 and 56), so
+    that x / scale lands on every e4m3 value and every tie between two (ties go
+    to the even code, subnormals included), with both signs; a group at a
+    scale that is not a power of two; a group of zeros (scale from the 1e-10
+    floor); and tiny values (per-token-group quantisation, modular_kernel.py
+    page, and the worst-tokens page's batched rows)."""
+    wl = WORKLOADS["decode_fp8_m64"].replace(M=64, K=512, I=128, E=4, topk=1, capacity=64)
+    edges = _e4m3_rounding_edges()
+    rng = np.random.default_rng(5)
+    x = np.zeros((wl.M, wl.K), np.float32)
+    for m in range(wl.M):
+        sel = rng.permutation(edges.size)[:127]
+        sign = np.where(rng.random(127) < 0.5, -1.0, 1.0)
+        x[m, 0:127] = edges[sel] * sign                        # group 0: scale 1
+        x[m, 127] = 448.0
+        x[m, 128:255] = edges[sel] * sign / 8.0                # group 1: scale 2^-3
+        x[m, 255] = -56.0
+        x[m, 256:384] = rng.standard_normal(128) * 37.0        # group 2: any scale
+        if m % 2 == 0:
+            x[m, 384:512] = 0.0                                # group 3: all zero ...
+        else:
+            x[m, 384:512] = rng.standard_normal(128) * 1e-5    # ... or tiny
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    assert np.array_equal(xb.float().numpy()[:, :256], x[:, :256])   # the edges are exact in bf16
+    ids, _ = _ids_from_oracle(wl)
+    p = U.problem(wl)
+    L = moe.workspace_layout(p)
+    ws = moe.empty_workspace(p)
+    cap, E, K = wl.capacity, wl.E, wl.K
+    a_out = torch.full((E, cap, K), 0x7F, dtype=torch.uint8, device="cuda")
+    a_scale = torch.full((E, cap, K // 128), -1.0, device="cuda")
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    print(f"  fp8 quantiser edges: M={wl.M} K={K}", flush=True)
+    moe.moe_prepare(p, xb.cuda(), torch.from_numpy(ids).cuda(), a_out, a_scale, counts, ws)
+    torch.cuda.synchronize()
+    rinv = U.ws_view(ws, L.inv, wl.M * wl.topk).cpu().numpy()
+    kept = rinv >= 0
+    assert kept.all()
+    rows, toks = rinv, np.arange(wl.M * wl.topk) // wl.topk
+    q, sc = oracle.quant_g128(xb.float().numpy())
+    assert (sc[:, 0] == 1.0).all() and (sc[:, 1] == 0.125).all()
+    np.testing.assert_array_equal(a_out.cpu().reshape(E * cap, K).numpy()[rows], q[toks])
+    np.testing.assert_array_equal(a_scale.cpu().reshape(E * cap, K // 128).numpy()[rows], sc[toks])
+
+
 def test_prepare_flags_bad_ids():
     wl = WORKLOADS["tiny_fp32"]
     ids, _ = _ids_from_oracle(wl)
