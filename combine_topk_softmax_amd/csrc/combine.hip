@@ -9,7 +9,9 @@
 // another expert-parallel shard holds, adds nothing.  With the router weight
 // applied on the input the outputs are added unweighted.
 //
-// HBM-bound: one block per token, 8 outputs per thread and pass.  The picks
+// HBM-bound: one block per token (and column range: a small batch spreads
+// each token's columns over several blocks so that every CU has work), 8
+// outputs per thread and pass.  The picks
 // go in groups of up to 8: their slots and weights first, then every row's
 // 16-byte loads at once (a dropped pick loads nothing), then the fp32 sums in
 // j order, so a thread keeps up to 8 rows in flight instead of one.  Each
@@ -28,7 +30,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ y, c
                                                       const int32_t *__restrict__ inv, int rows_from_inv,
                                                       int K, int k, T *__restrict__ out) {
   const int m = blockIdx.x;
-  for (int c = threadIdx.x * 8; c < K; c += 256 * 8) {
+  for (int c = (blockIdx.y * 256 + threadIdx.x) * 8; c < K; c += 256 * 8 * gridDim.y) {
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int j0 = 0; j0 < k; j0 += kGroup) {
       int64_t row[kGroup];
@@ -111,7 +113,7 @@ __global__ __launch_bounds__(256) void combine_split_kernel(const float *__restr
                                                             const int32_t *__restrict__ inv, int K, int k,
                                                             uint16_t *__restrict__ out) {
   const int m = blockIdx.x;
-  for (int c = threadIdx.x * 8; c < K; c += 256 * 8) {
+  for (int c = (blockIdx.y * 256 + threadIdx.x) * 8; c < K; c += 256 * 8 * gridDim.y) {
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int j0 = 0; j0 < k; j0 += kSplitGroup) {
       int64_t slot[kSplitGroup];
@@ -171,10 +173,15 @@ __global__ __launch_bounds__(256) void combine_split_kernel(const float *__restr
 
 }  // namespace
 
+// Blocks per token: one for large batches, else one per 2048 columns.
+static unsigned combine_col_blocks(const moe_problem &p) {
+  return p.M >= 1024 ? 1u : (unsigned)((p.K + 2047) / 2048);
+}
+
 hipError_t launch_combine_split(const moe_problem &p, const float *part, int S, int64_t stride,
                                 const float *topk_w, const int32_t *inv, void *out, hipStream_t s) {
   if (p.act_dtype != MOE_DTYPE_BF16 || !inv) return hipErrorInvalidValue;
-  dim3 grid((unsigned)p.M), block(256);
+  dim3 grid((unsigned)p.M, combine_col_blocks(p)), block(256);
   combine_split_kernel<<<grid, block, 0, s>>>(part, S, stride, topk_w, inv, (int)p.K, (int)p.topk,
                                               (uint16_t *)out);
   return hipGetLastError();
@@ -182,7 +189,7 @@ hipError_t launch_combine_split(const moe_problem &p, const float *part, int S, 
 
 hipError_t launch_combine(const moe_problem &p, const void *fused_out, const float *topk_w,
                           const int32_t *inv, bool rows_from_inv, void *out, hipStream_t s) {
-  dim3 grid((unsigned)p.M), block(256);
+  dim3 grid((unsigned)p.M, combine_col_blocks(p)), block(256);
   const int K = (int)p.K, k = (int)p.topk, r = rows_from_inv ? 1 : 0;
   if (p.act_dtype == MOE_DTYPE_BF16)
     combine_kernel<uint16_t><<<grid, block, 0, s>>>((const uint16_t *)fused_out, topk_w, inv, r, K, k,

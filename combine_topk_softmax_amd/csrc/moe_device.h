@@ -111,27 +111,48 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
+// Wavefront reductions: the four 16-lane DPP rows reduce by row rotations
+// (no LDS traffic), then lanes 0, 16, 32 and 48 are read into scalar
+// registers and combined there, so every lane gets the same value.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+
+__device__ __forceinline__ float row_lane(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = row16_max(v);
+  return fmaxf(fmaxf(row_lane(v, 0), row_lane(v, 16)), fmaxf(row_lane(v, 32), row_lane(v, 48)));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += __uint_as_float(dpp_u32<0x128>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<0x124>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<0x122>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<0x121>(__float_as_uint(v)));
+  return (row_lane(v, 0) + row_lane(v, 16)) + (row_lane(v, 32) + row_lane(v, 48));
+}
+
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  return ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)v);
 }
 
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint32_t lo = __shfl_xor((uint32_t)v, o, 64);
-    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
-    uint64_t w = ((uint64_t)hi << 32) | lo;
-    v = w > v ? w : v;
-  }
-  return v;
+  v = max_u64(v, dpp_u64<0x128>(v));
+  v = max_u64(v, dpp_u64<0x124>(v));
+  v = max_u64(v, dpp_u64<0x122>(v));
+  v = max_u64(v, dpp_u64<0x121>(v));
+  auto lane_u64 = [&](int l) -> uint64_t {
+    return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), l) << 32) |
+           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  };
+  return max_u64(max_u64(lane_u64(0), lane_u64(16)), max_u64(lane_u64(32), lane_u64(48)));
 }
 
 // ------------------------------------------------------- packed weights
