@@ -73,6 +73,7 @@ constexpr int kGroupM = 8;              // row tiles per L2 group
 template <bool GATED, bool PACKED>
 __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(const GemmParams g, int n_tiles) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStage];
+  __shared__ int32_t Orow[GATED ? 1 : kRows];   // down: output row of each tile row (-1: none)
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = wv >> 2, wn = wv & 3;
@@ -249,6 +250,19 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(const GemmParams
   auto osw = [&](int r, int byte) { return r * kRowB + ((((byte >> 4) ^ (r & 7)) << 4) | (byte & 15)); };
   __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0): the last (unused) copies have landed
   __syncthreads();
+  // down: every tile row's output row, loaded once here (its latency runs
+  // under the staging below) instead of once per 16-byte store
+  int orow_t = -1;
+  if constexpr (!GATED) {
+    if (tid < T) {
+      const int64_t slot = row0 + tid;
+      orow_t = (int)slot;   // slots are int32 in the tile plan
+      if (g.out_perm) {
+        orow_t = g.out_perm[slot];
+        if (orow_t >= g.n_pairs) orow_t = -1;
+      }
+    }
+  }
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) {
 #pragma unroll
@@ -268,17 +282,17 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(const GemmParams
       }
     }
   }
+  if constexpr (!GATED) {
+    if (tid < kRows) Orow[tid] = orow_t;
+  }
   __syncthreads();
   const int64_t col0 = (int64_t)nt * kOutCols;
   for (int c = tid; c < T * kChunk; c += kThreads) {
     const int r = c / kChunk, off = (c - r * kChunk) * 16;
-    const int64_t slot = row0 + r;
-    int64_t orow = slot;
+    int64_t orow = row0 + r;
     if constexpr (!GATED) {
-      if (g.out_perm) {
-        orow = g.out_perm[slot];
-        if (orow < 0 || orow >= g.n_pairs) continue;
-      }
+      orow = Orow[r];
+      if (orow < 0) continue;
     }
     *reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(g.out) + (orow * g.ldo + col0) * 2 + off) =
         *reinterpret_cast<const u32x4 *>(smem + osw(r, off));
