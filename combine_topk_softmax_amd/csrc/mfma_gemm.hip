@@ -39,6 +39,13 @@
 //    issued in inline asm: the compiler cannot tell the four stages apart and
 //    would otherwise wait for every copy in flight before each fragment read,
 //    and a workgroup fence would do the same, so the barrier is a bare one;
+//  * addressing stays out of the vector registers: the weights are read
+//    through a buffer resource on the expert's block (a per-lane 32-bit
+//    offset plus scalar block and step offsets), the A copies take a scalar
+//    base plus one 32-bit row offset per lane, and the wavefront index is
+//    made uniform, which leaves room for a sub-step's eight A fragments to be
+//    read together ahead of its MFMAs (plus two of the next sub-step's during
+//    the last MFMAs) instead of two at a time just before their MFMAs;
 //  * all loads are unconditional (rows past the count read a valid row whose
 //    products are never stored);
 //  * work items are dealt out XCD by XCD and, inside an XCD's range, grouped
@@ -48,7 +55,9 @@
 // Measured on one MI355X on the skewed prefill's expert shapes and tile plan
 // (567 row tiles of 256, packed weights), same box and run, against the
 // previous kernel (both operands staged global -> registers -> LDS, 32x32x16
-// MFMAs): gated GEMM 3.52-3.64 -> 3.06 ms, down GEMM 1.91-1.99 -> 1.72 ms.
+// MFMAs): gated GEMM 3.52-3.64 -> 3.06 ms, down GEMM 1.91-1.99 -> 1.72 ms;
+// the scalar addressing and early fragment reads then took 2.99 -> 2.87 ms
+// and 1.74 -> 1.70 ms.
 // With both operands made cache-resident the same loop took 3.04 ms: the
 // loads are hidden, and the MFMA pipes are busy about half of the time.
 #include "moe_device.h"
@@ -67,6 +76,7 @@ constexpr int kStep = 128;              // bytes of K per step (64 bf16)
 constexpr int kStages = 4;              // A stages in LDS
 constexpr int kStage = kRows * kStep;   // 32 KB
 constexpr int kGroupM = 8;              // row tiles per L2 group
+constexpr int kPrefetch = 2;            // fragments of the second sub-step read early
 
 #define MOE_LP(p) ((__attribute__((address_space(3))) void *)(p))
 
@@ -75,7 +85,9 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(const GemmParams
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStage];
   __shared__ int32_t Orow[GATED ? 1 : kRows];   // down: output row of each tile row (-1: none)
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  // the wavefront index is uniform: block and step offsets derived from it
+  // stay in scalar registers
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv >> 2, wn = wv & 3;
   const bool dense = g.t.dense_rows > 0;
   const int m_tiles = dense ? (g.t.dense_rows + kRows - 1) / kRows : *g.t.tile_count;
@@ -112,41 +124,50 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(const GemmParams
   // A copies: wavefront wv fills rows wv*32 + 8j + lane/8 (j < 4) of each
   // stage; lane l writes slot l % 8 of its row, which holds global chunk
   // (l % 8) ^ (row & 7) = (l % 8) ^ (l / 8).  Rows past the tile's count and
-  // padding slots read row 0 instead: an A row only feeds its own output row,
-  // and the epilogue writes nothing for those.
+  // padding slots read the base row instead: an A row only feeds its own
+  // output row, and the epilogue writes nothing for those.  Row offsets are
+  // 32-bit from a wavefront-uniform base: the tile's first slot row when A
+  // is indexed by slot, the start of A when rows are gathered through perm.
   const int rr = lane >> 3, cg = (lane & 7) ^ rr;
-  const uint8_t *a_src[4];
+  const uint8_t *a_base = reinterpret_cast<const uint8_t *>(g.a) + (g.perm ? 0 : row0 * row_bytes);
+  uint32_t a_off[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int q = wv * 32 + 8 * j + rr;
-    a_src[j] = reinterpret_cast<const uint8_t *>(g.a) + cg * 16;
+    a_off[j] = (uint32_t)(cg * 16);
     if (q < T) {
-      const int64_t s = row0 + q;
-      int64_t arow = s;
+      int64_t arow = q;
       if (g.perm) {
-        const int f = g.perm[s];
+        const int f = g.perm[row0 + q];
         arow = (f >= 0 && f < g.n_pairs) ? f / g.topk : -1;
       }
-      if (arow >= 0) a_src[j] = reinterpret_cast<const uint8_t *>(g.a) + arow * row_bytes + cg * 16;
+      if (arow >= 0) a_off[j] = (uint32_t)(arow * row_bytes) + (uint32_t)(cg * 16);
     }
   }
   // B: this wavefront's four 16-row blocks -- gated: gate, gate, up, up (act
   // columns wn*32 + 16 (nb % 2)); down: four adjacent blocks of outputs.
+  // Loaded through a buffer resource on expert e's weights (32-bit offsets:
+  // a per-lane one, and wavefront-uniform block and step offsets).
   auto brow = [&](int nb) -> int64_t {
     if (GATED) return (nb < 2 ? (int64_t)0 : g.half_n) + (int64_t)nt * 128 + wn * 32 + (nb & 1) * 16;
     return (int64_t)nt * kCols + wn * 64 + nb * 16;
   };
   const int bc = 2 * (lane >> 4);   // lane's first 16-byte chunk of a K-step
-  // a small per-lane offset, plus wavefront-uniform block and step offsets
+  const int64_t e_bytes = g.Nw * row_bytes;
   const uint32_t b_lane = PACKED ? (uint32_t)(packed_piece(pg, e, brow(0) + (lane & 15), 0, bc) -
                                               packed_piece(pg, e, brow(0), 0, 0))
                                  : (uint32_t)((lane & 15) * row_bytes + bc * 16);
-  int64_t b_off[4];
+  uint32_t b_off[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb)
-    b_off[nb] = PACKED ? packed_piece(pg, e, brow(nb), 0, 0) : ((int64_t)e * g.Nw + brow(nb)) * row_bytes;
-  const uint8_t *const wb = reinterpret_cast<const uint8_t *>(g.w);
-  constexpr int64_t kPstep = PACKED ? 1024 : 16;   // the second sub-step of a K-step
+    b_off[nb] = (uint32_t)((PACKED ? packed_piece(pg, e, brow(nb), 0, 0) : ((int64_t)e * g.Nw + brow(nb)) * row_bytes) -
+                           (int64_t)e * e_bytes);
+  // raw buffer (stride 0) over the expert's e_bytes (< 2^31, checked on the
+  // host); word 3 gives the 32-bit data format that raw loads require
+  const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(reinterpret_cast<const uint8_t *>(g.w)) + (int64_t)e * e_bytes, (short)0,
+      (int)e_bytes, 0x00020000);
+  constexpr uint32_t kPstep = PACKED ? 1024 : 16;   // the second sub-step of a K-step
 
   f32x4 acc[8][4];
 #pragma unroll
@@ -157,41 +178,36 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(const GemmParams
 
   // LDS byte address of this wavefront's first copy row in stage 0
   const uint32_t lds0 = (uint32_t)(uintptr_t)MOE_LP(smem) + (uint32_t)(wv * 32) * kStep;
-  // A of K-step ks into `stage`.  Issued in asm: the compiler's wait counting
-  // cannot tell the stages apart and would wait for every copy in flight
-  // before each fragment read; the copies' own waits are the explicit vmcnt
-  // before each barrier.
+  // A of K-step ks into `stage` (scalar base + the 32-bit row offsets).
+  // Issued in asm: the compiler's wait counting cannot tell the four stages
+  // apart and would wait for every copy in flight before each fragment read;
+  // the copies' own waits are the explicit vmcnt before each barrier.
   auto copy_a = [&](int stage, int ks) {
+    const uint8_t *src = a_base + (int64_t)ks * kStep;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(stage * kStage + 8 * j * kStep));
-      const uint8_t *src = a_src[j] + (int64_t)ks * kStep;
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_nop 0"
-                   :: "s"(m0v), "v"(src) : "memory", "m0");
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_nop 0"
+                   :: "s"(m0v), "v"(a_off[j]), "s"(src) : "memory", "m0");
     }
   };
   // B of sub-step t (K-step t / 2, sub-step t % 2) into `slot`
   auto load_b = [&](int slot, int t) {
     const int ks = min(t >> 1, nk - 1), p = t & 1;
+    const uint32_t so = (uint32_t)ks * (uint32_t)kstride + (uint32_t)p * kPstep;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
-      bf[slot][nb] = *reinterpret_cast<const bf16x8 *>(wb + (b_off[nb] + (int64_t)ks * kstride + p * kPstep) + b_lane);
+      bf[slot][nb] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, b_lane, b_off[nb] + so, 0));
   };
-  // one 32-element sub-step p from A `stage` and B `slot`
-  auto substep = [&](int stage, int slot, int p) {
-    const uint8_t *As = smem + stage * kStage;
-    const int c = bc + p;
-    bf16x8 af[8];
+  // A fragment of 32-row block mb, sub-step p: lane l reads row
+  // wm*128 + 16 mb + l % 16 of the stage, 16-byte chunk bc + p swizzled by the
+  // row's low bits (= l % 8); one base per sub-step, the rest immediate offsets
+  uint32_t a_rd[2];
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-      const int r = wm * 128 + mb * 16 + (lane & 15);
-      af[mb] = *reinterpret_cast<const bf16x8 *>(As + r * kStep + ((c ^ (r & 7)) << 4));
-    }
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb], bf[slot][nb], acc[mb][nb], 0, 0, 0);
+  for (int p = 0; p < 2; ++p)
+    a_rd[p] = (uint32_t)((wm * 128 + (lane & 15)) * kStep + (((bc + p) ^ (lane & 7)) << 4));
+  auto read_a = [&](int stage, int p, int mb) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8 *>(smem + stage * kStage + mb * 16 * kStep + a_rd[p]);
   };
 
   // Prologue: A steps 0-2 copying, B sub-steps 0-2.  The order matters:
@@ -206,7 +222,12 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(const GemmParams
   // compile-time): each sub-step t first issues the B loads of sub-step t + 3
   // into the slot sub-step t - 1 freed; the A copy of ks + 3 goes out at the
   // end, into the stage the barrier released.  Steps past the last re-copy
-  // and reload the last one instead of branching around the loads.
+  // and reload the last one instead of branching around the loads.  A
+  // sub-step's eight fragment reads are issued together ahead of its MFMAs,
+  // and the first kPrefetch of the second sub-step's go out during the
+  // first sub-step's last MFMAs, so neither sub-step starts on a bare LDS
+  // latency (the compiler would otherwise read each pair of fragments just
+  // before its MFMAs).
   auto kstep = [&](auto ST_, int ks) {
     constexpr int ST = decltype(ST_)::value, S0 = (2 * ST) & 3, S1 = (2 * ST + 1) & 3;
     // vmcnt(16): all but the last 16 loads (the previous step's B loads and
@@ -217,12 +238,32 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(const GemmParams
     asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
     load_b((S0 + 3) & 3, 2 * ks + 3);
+    bf16x8 af[8], pf[kPrefetch];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) af[mb] = read_a(ST, 0, mb);
     __builtin_amdgcn_sched_barrier(0);
-    substep(ST, S0, 0);
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb], bf[S0][nb], acc[mb][nb], 0, 0, 0);
+      if (mb == 5) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < kPrefetch; ++i) pf[i] = read_a(ST, 1, i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
     load_b((S1 + 3) & 3, 2 * ks + 4);
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) af[mb] = mb < kPrefetch ? pf[mb] : read_a(ST, 1, mb);
     __builtin_amdgcn_sched_barrier(0);
-    substep(ST, S1, 1);
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb], bf[S1][nb], acc[mb][nb], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
     copy_a((ST + 3) & 3, min(ks + 3, nk - 1));
   };
@@ -303,10 +344,14 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(const GemmParams
 
 int mfma_gemm_tile_rows() { return kRows; }
 
-bool mfma_gemm_fits(int w_dtype, int act_dtype, int64_t K, int64_t I) {
+bool mfma_gemm_fits(int w_dtype, int act_dtype, int64_t K, int64_t I, int64_t M) {
   // bf16 in and out; gated column tiles of 128 act columns, down column tiles
-  // of 256 outputs, an even number of 64-element K-steps on both reductions.
-  return w_dtype == MOE_DTYPE_BF16 && act_dtype == MOE_DTYPE_BF16 && I % 128 == 0 && K % 256 == 0;
+  // of 256 outputs, an even number of 64-element K-steps on both reductions;
+  // 32-bit offsets within one expert's weights (2I x K) and within the M
+  // token rows that the gated GEMM gathers.
+  const int64_t lim = (int64_t)1 << 31;
+  return w_dtype == MOE_DTYPE_BF16 && act_dtype == MOE_DTYPE_BF16 && I % 128 == 0 && K % 256 == 0 &&
+         2 * I * K * 2 < lim && M * K * 2 < lim;
 }
 
 int mfma_gemm_n_tiles(GemmKind kind, int64_t Nw) { return (int)(kind == kGemmGatedAct ? Nw / 256 : Nw / kCols); }

@@ -189,7 +189,7 @@ int gemm_tile_rows(const moe_problem &p, const moe_ws_layout &L) {
   const int64_t I = p.N / 2;
   const int64_t local_pairs = local_pairs_of(p, p.M * p.topk);
   const bool streaming = streaming_of(p, local_pairs);
-  const bool big = !streaming && mfma_gemm_fits(p.w_dtype, p.act_dtype, p.K, I);
+  const bool big = !streaming && mfma_gemm_fits(p.w_dtype, p.act_dtype, p.K, I, p.M);
   const bool wide = streaming && stream_gemm_gated_wide(p.w_dtype, p.E, local_pairs, p.K, I);
   return wide ? stream_gemm_wide_tile_rows() : streaming ? stream_gemm_tile_rows(p.w_dtype)
                                              : big       ? mfma_gemm_tile_rows()
@@ -290,7 +290,7 @@ moe_status do_experts(const moe_problem &p, const void *a, const float *a_scale,
   const bool streaming = streaming_of(p, local_pairs);
   // Past that point the GEMMs are bound by the matrix cores: 256 x 256 tiles
   // where the shapes allow, the general 128 x 128 kernel otherwise.
-  const bool big = !streaming && mfma_gemm_fits(p.w_dtype, p.act_dtype, p.K, I);
+  const bool big = !streaming && mfma_gemm_fits(p.w_dtype, p.act_dtype, p.K, I, p.M);
   const bool wide = streaming && stream_gemm_gated_wide(p.w_dtype, p.E, local_pairs, p.K, I);
   // (a small batch's counting kernel already wrote the plan)
   if (!planned)
@@ -410,7 +410,7 @@ moe_status do_shared(const moe_problem &p, const void *x, const void *w1, const 
   g1.half_n = Is;
   g1.act = p.activation;
   g1.t = gt;
-  const bool big = mfma_gemm_fits(p.act_dtype, p.act_dtype, p.K, Is);
+  const bool big = mfma_gemm_fits(p.act_dtype, p.act_dtype, p.K, Is, p.M);
   if (big)
     MOE_HIP(launch_mfma_gemm(kGemmGatedAct, g1, mfma_gemm_n_tiles(kGemmGatedAct, g1.Nw), s));
   else

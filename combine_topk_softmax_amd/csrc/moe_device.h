@@ -297,7 +297,7 @@ hipError_t launch_stream_gemm(int w_dtype, int out_dtype, GemmKind kind, const G
 // Compute-bound variant (bf16, many rows per expert): 256-row tiles; gated
 // tiles cover 128 act columns, down tiles 256 output columns.
 int mfma_gemm_tile_rows();
-bool mfma_gemm_fits(int w_dtype, int act_dtype, int64_t K, int64_t I);
+bool mfma_gemm_fits(int w_dtype, int act_dtype, int64_t K, int64_t I, int64_t M);
 int mfma_gemm_n_tiles(GemmKind kind, int64_t Nw);
 hipError_t launch_mfma_gemm(GemmKind kind, const GemmParams &g, int n_tiles, hipStream_t s);
 hipError_t launch_pack_weights(const void *src, void *dst, int64_t E, int64_t Nw, int64_t row_bytes, bool gated,
