@@ -10,28 +10,32 @@
 // laid out for gfx950's matrix cores when flops, not weight bytes, set the
 // time:
 //
-//  * a workgroup computes a 256-row x 256-column tile (rows: one expert's
+//  * a workgroup computes a 128-row x 256-column tile (rows: one expert's
 //    slots from the device tile plan; columns: 128 gate + the matching 128 up
-//    weight rows, or 256 output columns) with 8 wavefronts in a 2 x 4 grid,
-//    each owning 128 x 64 as 8 x 4 blocks of v_mfma_f32_16x16x32_bf16 (128
-//    fp32 accumulators per lane, two wavefronts per SIMD);
+//    weight rows, or 256 output columns) with 4 wavefronts side by side, each
+//    owning 128 x 64 as 8 x 4 blocks of v_mfma_f32_16x16x32_bf16 (128 fp32
+//    accumulators per lane).  Two workgroups share a CU, one wavefront of
+//    each per SIMD: while one waits at its K-step barrier, the other's MFMAs
+//    keep the SIMD busy (with one 8-wavefront workgroup per CU every SIMD
+//    idled at each barrier, about a fifth of the K-step);
 //  * the activation rows (A) are copied global -> LDS by the LDS DMA
 //    (global_load_lds_dwordx4: no staging registers, no LDS store
-//    instructions) into 4 stages of 256 rows x 128 bytes (64 elements of K),
+//    instructions) into 4 stages of 128 rows x 128 bytes (64 elements of K),
 //    the 16-byte chunks of a row XOR-swizzled by the row's low bits so that
 //    the fragment reads of 8 consecutive rows hit distinct banks.  The copy
 //    of K-step s + 3 is issued at the end of step s, into the stage the
 //    step's barrier released, so it has more than two K-steps to land;
 //  * the weights (B) never touch LDS: each wavefront loads its own 16-row
-//    fragments straight from global memory into registers, 1.5 K-steps ahead
+//    fragments (each loaded once per workgroup) straight from global memory
+//    into registers, 1.5 K-steps ahead
 //    through a ring of four sub-step slots.  With the packed weight layout a
 //    wavefront's fragment of one 32-element sub-step is one contiguous 1 KB
 //    (the layout stores exactly this lane order: lane l holds row l % 16, K
 //    elements 16 (l / 16) + 8 p of each 64-element step, p the sub-step), so
 //    every B load is fully coalesced; A fragments are read from LDS in the
 //    same K order.  Against staging both operands through LDS this moves 37%
-//    fewer LDS bytes per flop, and it spreads the global loads over all 8
-//    wavefronts (one wavefront's vector-memory throughput is limited: a probe
+//    fewer LDS bytes per flop, and it spreads the global loads over all the
+//    wavefronts of a CU (one wavefront's vector-memory throughput is limited: a probe
 //    of plain 16-byte loads from L2 gave 32 GB/s per CU with 4 wavefronts per
 //    CU, 76 GB/s with 8);
 //  * one barrier per K-step, after an explicit `s_waitcnt vmcnt(16)` (all but
@@ -52,12 +56,13 @@
 //    eight row tiles at a time per column tile, so the workgroups resident on
 //    one XCD share both activation rows and weight panels through its L2.
 //
-// Measured on one MI355X on the skewed prefill's expert shapes and tile plan
-// (567 row tiles of 256, packed weights), same box and run, against the
-// previous kernel (both operands staged global -> registers -> LDS, 32x32x16
-// MFMAs): gated GEMM 3.52-3.64 -> 3.06 ms, down GEMM 1.91-1.99 -> 1.72 ms;
-// the scalar addressing and early fragment reads then took 2.99 -> 2.87 ms
-// and 1.74 -> 1.70 ms.
+// Measured on one MI355X on the skewed prefill's expert shapes (packed
+// weights), same box and run, against the previous kernel (one 256-row tile
+// per CU, both operands staged global -> registers -> LDS, 32x32x16 MFMAs):
+// gated GEMM 3.52-3.64 -> 3.06 ms, down GEMM 1.91-1.99 -> 1.72 ms; the scalar
+// addressing and early fragment reads then took 2.99 -> 2.87 ms and 1.74 ->
+// 1.70 ms, and two 128-row workgroups per CU in place of one 256-row
+// workgroup of 8 wavefronts (2 x 4) 2.87 -> 2.75 ms and 1.69 -> 1.64 ms.
 // With both operands made cache-resident the same loop took 3.04 ms: the
 // loads are hidden, and the MFMA pipes are busy about half of the time.
 #include "moe_device.h"
@@ -69,26 +74,26 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 512;
-constexpr int kRows = 256;              // tile rows (slots)
+constexpr int kThreads = 256;
+constexpr int kRows = 128;              // tile rows (slots)
 constexpr int kCols = 256;              // tile columns (weight rows)
 constexpr int kStep = 128;              // bytes of K per step (64 bf16)
 constexpr int kStages = 4;              // A stages in LDS
-constexpr int kStage = kRows * kStep;   // 32 KB
+constexpr int kStage = kRows * kStep;   // 16 KB
 constexpr int kGroupM = 8;              // row tiles per L2 group
 constexpr int kPrefetch = 2;            // fragments of the second sub-step read early
 
 #define MOE_LP(p) ((__attribute__((address_space(3))) void *)(p))
 
 template <bool GATED, bool PACKED>
-__global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(const GemmParams g, int n_tiles) {
+__global__ __launch_bounds__(kThreads, 2) void mfma_gemm_kernel(const GemmParams g, int n_tiles) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStage];
   __shared__ int32_t Orow[GATED ? 1 : kRows];   // down: output row of each tile row (-1: none)
 
   // the wavefront index is uniform: block and step offsets derived from it
   // stay in scalar registers
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wv >> 2, wn = wv & 3;
+  const int wn = wv;   // the wavefront's 64 columns of the tile
   const bool dense = g.t.dense_rows > 0;
   const int m_tiles = dense ? (g.t.dense_rows + kRows - 1) / kRows : *g.t.tile_count;
   const int total = m_tiles * n_tiles;
@@ -199,13 +204,13 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(const GemmParams
     for (int nb = 0; nb < 4; ++nb)
       bf[slot][nb] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, b_lane, b_off[nb] + so, 0));
   };
-  // A fragment of 32-row block mb, sub-step p: lane l reads row
-  // wm*128 + 16 mb + l % 16 of the stage, 16-byte chunk bc + p swizzled by the
+  // A fragment of 16-row block mb, sub-step p: lane l reads row
+  // 16 mb + l % 16 of the stage, 16-byte chunk bc + p swizzled by the
   // row's low bits (= l % 8); one base per sub-step, the rest immediate offsets
   uint32_t a_rd[2];
 #pragma unroll
   for (int p = 0; p < 2; ++p)
-    a_rd[p] = (uint32_t)((wm * 128 + (lane & 15)) * kStep + (((bc + p) ^ (lane & 7)) << 4));
+    a_rd[p] = (uint32_t)((lane & 15) * kStep + (((bc + p) ^ (lane & 7)) << 4));
   auto read_a = [&](int stage, int p, int mb) -> bf16x8 {
     return *reinterpret_cast<const bf16x8 *>(smem + stage * kStage + mb * 16 * kStep + a_rd[p]);
   };
@@ -308,7 +313,7 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_gemm_kernel(const GemmParams
   for (int mb = 0; mb < 8; ++mb) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = wm * 128 + mb * 16 + (lane >> 4) * 4 + i;
+      const int r = mb * 16 + (lane >> 4) * 4 + i;
       if constexpr (GATED) {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {

@@ -288,7 +288,7 @@ moe_status do_experts(const moe_problem &p, const void *a, const float *a_scale,
   int32_t *perm = standard ? at<int32_t>(ws, L.perm) : nullptr;
   const int64_t local_pairs = local_pairs_of(p, p.M * p.topk);
   const bool streaming = streaming_of(p, local_pairs);
-  // Past that point the GEMMs are bound by the matrix cores: 256 x 256 tiles
+  // Past that point the GEMMs are bound by the matrix cores: 128 x 256 tiles
   // where the shapes allow, the general 128 x 128 kernel otherwise.
   const bool big = !streaming && mfma_gemm_fits(p.w_dtype, p.act_dtype, p.K, I, p.M);
   const bool wide = streaming && stream_gemm_gated_wide(p.w_dtype, p.E, local_pairs, p.K, I);

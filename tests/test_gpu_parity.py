@@ -220,16 +220,16 @@ SMALL = {
     "fp8_batched": WORKLOADS["decode_fp8_m64"].replace(M=90, K=384, I=256, E=5, topk=2, capacity=90),
     "fp8_standard": WORKLOADS["decode_fp8_m64"].replace(M=90, K=256, I=256, E=6, topk=3,
                                                         format=FORMAT_STANDARD, capacity=0),
-    # more rows per expert than one weight-streaming tile: 256 x 256 MFMA tiles,
+    # more rows per expert than one weight-streaming tile: 128 x 256 MFMA tiles,
     # several row tiles per expert plus a ragged last one, 2 column tiles
     "bf16_mfma": WORKLOADS["mixtral_bf16"].replace(M=700, K=512, I=256, E=4, topk=2, renormalize=False,
                                                    logits_dist="normal"),
     "bf16_mfma_batched": WORKLOADS["mixtral_bf16"].replace(M=600, K=256, I=128, E=3, topk=2,
                                                            format=FORMAT_BATCHED, capacity=600,
                                                            logits_dist="normal"),
-    # 256 x 256 MFMA tiles past one L2 group of row tiles: 12 row tiles (a
-    # whole group of 8 and a partial one of 4) x 2 column tiles, and 18 row
-    # tiles (two whole groups and a partial one of 2) with Zipf routing
+    # 128 x 256 MFMA tiles past one L2 group of row tiles: about 20 row tiles
+    # (two whole groups of 8 and a partial one) x 2 column tiles, and about 33
+    # row tiles (four whole groups and a partial one)
     "bf16_mfma_groups": WORKLOADS["mixtral_bf16"].replace(M=1200, K=512, I=256, E=4, topk=2, renormalize=False,
                                                           logits_dist="normal"),
     "bf16_mfma_18tiles": WORKLOADS["mixtral_bf16"].replace(M=2000, K=256, I=256, E=3, topk=2, renormalize=False,
@@ -792,7 +792,7 @@ GELU_CASES = {
 @pytest.mark.parametrize("name", list(GELU_CASES))
 def test_gelu_forward_parity(name):
     """gelu_and_mul in every gated epilogue (tiled, streaming with fp8
-    re-quantisation, 256x256 MFMA, shared expert)."""
+    re-quantisation, 128x256 MFMA, shared expert)."""
     wl = GELU_CASES[name]
     d = make_inputs(wl, seed=31, device="cpu")
     out, sout, _, _ = U.run_forward(wl, U.to_cuda(d))
@@ -997,7 +997,7 @@ def test_chunked_forward_with_shard_map_and_bad_ids_flag():
 
 def _random_cases(n=24, seed=2024):
     """Seeded random small layers over dtype, format, scoring, activation and
-    ragged sizes, so that every grouped-GEMM kernel (weight streaming, 256x256
+    ragged sizes, so that every grouped-GEMM kernel (weight streaming, 128x256
     MFMA tiles, 128x128 tiles) meets shapes the named cases do not."""
     rng = np.random.default_rng(seed)
     cases = []

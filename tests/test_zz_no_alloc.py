@@ -15,7 +15,7 @@ pytestmark = pytest.mark.gpu
 
 # in call order: each later problem is smaller than the one before it
 CALLS = [
-    # 256 x 256 MFMA tiles (about 600 rows per expert)
+    # 128 x 256 MFMA tiles (about 600 rows per expert)
     ("bf16_mfma", WORKLOADS["mixtral_bf16"].replace(M=1200, K=512, I=256, E=4, topk=2, renormalize=False,
                                                     logits_dist="normal")),
     # weight streaming, with the shared expert on its aux stream
