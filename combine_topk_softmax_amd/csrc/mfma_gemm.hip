@@ -63,8 +63,10 @@
 // addressing and early fragment reads then took 2.99 -> 2.87 ms and 1.74 ->
 // 1.70 ms, and two 128-row workgroups per CU in place of one 256-row
 // workgroup of 8 wavefronts (2 x 4) 2.87 -> 2.75 ms and 1.69 -> 1.64 ms.
-// With both operands made cache-resident the same loop took 3.04 ms: the
-// loads are hidden, and the MFMA pipes are busy about half of the time.
+// With both operands made cache-resident (a timing copy of an earlier
+// schedule) the loop ran no faster: the loads are hidden.  The MFMA pipes are
+// busy 69% of the gated GEMM's cycles; the rest goes to the K-step barrier,
+// the copy issue and the empty rows of each expert's last, partial tile.
 #include "moe_device.h"
 
 namespace moe {
