@@ -21,7 +21,7 @@ namespace moe {
 namespace {
 
 constexpr int kMaxExperts = 1024;
-constexpr int kMaxChunks = 64;   // counting chunks per batch (the workspace layout keeps to it)
+constexpr int kMaxChunks = 256;   // counting chunks per batch (the workspace layout keeps to it)
 
 // ----------------------------------------------------------- histogram
 
@@ -85,18 +85,21 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t *__restrict__ chunk_
   if (e == 0 && clear_status) *status = 0;
   int run = 0;
   if (e < E) {
-    // the expert's column of chunk counts into registers first, so that the
-    // loads are in flight together rather than each behind the last store
-    int h[kMaxChunks];
+    // the expert's column of chunk counts, 64 at a time into registers, so
+    // that the loads are in flight together rather than each behind the
+    // last store
+    for (int c0 = 0; c0 < n_chunks; c0 += 64) {
+      int h[64];
 #pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c)
-      if (c < n_chunks) h[c] = chunk_hist[(int64_t)c * E + e];
+      for (int c = 0; c < 64; ++c)
+        if (c0 + c < n_chunks) h[c] = chunk_hist[(int64_t)(c0 + c) * E + e];
 #pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c)
-      if (c < n_chunks) {
-        chunk_hist[(int64_t)c * E + e] = run;
-        run += h[c];
-      }
+      for (int c = 0; c < 64; ++c)
+        if (c0 + c < n_chunks) {
+          chunk_hist[(int64_t)(c0 + c) * E + e] = run;
+          run += h[c];
+        }
+    }
     counts[e] = run;
     expert_num_tokens[e] = run;
   }

@@ -116,9 +116,12 @@ void layout(const moe_problem &p, moe_ws_layout &L) {
   const bool fp8 = fp8_path(p);
 
   L.perm_len = standard ? nc + E * (align - 1) : 0;
-  // pairs per counting chunk: at most 64 chunks, each one wavefront of the
-  // rank kernel, which steps through its chunk 64 pairs at a time
+  // pairs per counting chunk, each one wavefront of the rank kernel, which
+  // steps through its chunk 64 pairs at a time: 64 chunks of up to 512 pairs,
+  // then up to 256 chunks (the scan walks each expert's column of chunk
+  // counts, so more chunks pay only where the ranking is long)
   L.chunk = std::max<int64_t>(64, round_up((nc + 63) / 64, 64));
+  if (L.chunk > 512) L.chunk = std::max<int64_t>(512, round_up((nc + 255) / 256, 64));
   L.n_chunks = std::max<int64_t>(1, (nc + L.chunk - 1) / L.chunk);
   L.tile_rows = kTileRows;
   const int64_t tiled_rows = standard ? nc : std::min(n, E * cap);

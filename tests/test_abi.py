@@ -105,7 +105,7 @@ def test_workloads_validate_and_layout(name):
     else:
         assert L.act_rows == wl.E * wl.capacity
     assert L.max_tiles >= -(-n // 128)
-    assert L.n_chunks * L.chunk >= n and L.n_chunks <= 64
+    assert L.n_chunks * L.chunk >= n and L.n_chunks <= 256
 
 
 def test_validation_status_codes():
