@@ -313,23 +313,39 @@ __global__ __launch_bounds__(1024) void plan_tiles_kernel(const int32_t *__restr
       }
     }
   }
+  __shared__ int t0_sh[kMaxExperts], cnt_sh[kMaxExperts];
+  __shared__ int64_t seg_sh[kMaxExperts];
   const int nt = (cnt + tile_rows - 1) / tile_rows;
   const int t0 = block_exclusive_scan(nt, &total_sh);
   if (e < E) {
-    for (int i = 0; i < nt; ++i) {
-      const int t = t0 + i;
-      if (t >= max_tiles) {
-        atomicOr(status, MOE_DEVICE_CAPACITY_OVERFLOW);
-        break;
-      }
-      int32_t *d = tiles + (int64_t)t * 4;
-      d[0] = e;
-      d[1] = (int32_t)seg;
-      d[2] = i * tile_rows;
-      d[3] = min(tile_rows, cnt - i * tile_rows);
-    }
+    t0_sh[e] = t0;
+    cnt_sh[e] = cnt;
+    seg_sh[e] = seg;
   }
-  if (e == 0) tiles[(int64_t)max_tiles * 4] = min(total_sh, max_tiles);
+  __syncthreads();
+  // every thread writes tiles (an expert of many rows has many): tile t
+  // belongs to the last expert whose first tile is at or before t (experts
+  // without tiles share their first index with the next one)
+  const int total = total_sh;
+  for (int t = threadIdx.x; t < total; t += blockDim.x) {
+    if (t >= max_tiles) {
+      atomicOr(status, MOE_DEVICE_CAPACITY_OVERFLOW);
+      break;
+    }
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (t0_sh[mid] <= t) lo = mid;
+      else hi = mid - 1;
+    }
+    const int i = t - t0_sh[lo];
+    int32_t *d = tiles + (int64_t)t * 4;
+    d[0] = lo;
+    d[1] = (int32_t)seg_sh[lo];
+    d[2] = i * tile_rows;
+    d[3] = min(tile_rows, cnt_sh[lo] - i * tile_rows);
+  }
+  if (e == 0) tiles[(int64_t)max_tiles * 4] = min(total, max_tiles);
 }
 
 // -------------------------------------------------- small batches, one block
