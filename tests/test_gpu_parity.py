@@ -1170,3 +1170,56 @@ def test_dbo_graph_replay_matches_eager():
         torch.cuda.synchronize()
         assert torch.equal(got, ref), r
         assert torch.equal(sgot, sref), r
+
+
+PLAN_CASES = {
+    # the large-batch counting (up to 256 chunks) and plan kernels: 131K Zipf
+    # pairs whose largest expert has about 130 row tiles, and 32K pairs over
+    # 256 experts
+    # (K and I cut down: the routing and so the plan do not depend on them)
+    "skewed_full": WORKLOADS["skewed_bf16"].replace(K=256, I=128),
+    "dsv3_full": WORKLOADS["dsv3_bf16"].replace(K=256, I=128, shared_I=0),
+    # a small batch: the one-block counting kernel writes the plan
+    "mixtral_small": WORKLOADS["mixtral_bf16"].replace(M=300, K=256, I=128, logits_dist="normal"),
+    # BatchedExperts rows (segment e * capacity)
+    "decode_m256": WORKLOADS["decode_fp8_m256"].replace(K=512, I=256),
+    # experts without pairs first, in the middle and last (their logits pushed
+    # down), past the small-batch size
+    "empty_experts": WORKLOADS["mixtral_bf16"].replace(M=3000, K=256, I=256, E=16, topk=2,
+                                                       renormalize=False, logits_dist="normal"),
+}
+
+
+@pytest.mark.parametrize("name", list(PLAN_CASES))
+def test_tile_plan_matches_counts(name):
+    """The grouped GEMMs' tile plan, read from the workspace after a forward
+    pass, against the one the counts define: for every expert in order,
+    ceil(count / rows) tiles of (expert, segment start, first row, rows), with
+    rows the plan's tile height (the largest tile) and the count clipped to
+    the capacity in the batched format; the tile count after them."""
+    wl = PLAN_CASES[name]
+    d = make_inputs(wl, seed=23, device="cpu")
+    if name == "empty_experts":
+        for e in (0, 1, 7, wl.E - 2, wl.E - 1):
+            d["logits"][:, e] = -1e4
+    out, _, ws, p = U.run_forward(wl, U.to_cuda(d))
+    torch.cuda.synchronize()
+    L = moe.workspace_layout(p)
+    ids = U.ws_view(ws, L.topk_ids, wl.M * wl.topk).cpu().numpy()
+    counts = np.bincount(ids, minlength=wl.E)[: wl.E]
+    if name == "empty_experts":
+        assert counts[[0, 1, 7, wl.E - 2, wl.E - 1]].sum() == 0 and counts.sum() == wl.M * wl.topk
+    ntile = U.ws_view(ws, L.tiles + 4 * 4 * L.max_tiles, 1).item()
+    tiles = U.ws_view(ws, L.tiles, 4 * ntile).cpu().numpy().reshape(ntile, 4)
+    rows = int(tiles[:, 3].max())
+    if U.batched(wl):
+        seg = np.arange(wl.E) * wl.capacity
+        cnt = np.minimum(counts, wl.capacity)
+    else:
+        seg = U.ws_view(ws, L.offsets, wl.E).cpu().numpy()
+        cnt = counts
+    ref = [(e, seg[e], i * rows, min(rows, cnt[e] - i * rows))
+           for e in range(wl.E) for i in range(-(-int(cnt[e]) // rows))]
+    print(f"  plan {name}: {ntile} tiles of {rows} rows, largest expert {cnt.max()} rows", flush=True)
+    assert ntile == len(ref) <= L.max_tiles
+    np.testing.assert_array_equal(tiles, np.array(ref, dtype=np.int64).reshape(-1, 4))
