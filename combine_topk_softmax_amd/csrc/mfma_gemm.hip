@@ -53,7 +53,7 @@
 //  * all loads are unconditional (rows past the count read a valid row whose
 //    products are never stored);
 //  * work items are dealt out XCD by XCD and, inside an XCD's range, grouped
-//    16 (gated) or 8 (down) row tiles at a time per column tile, so the
+//    16 (gated) or 6 (down) row tiles at a time per column tile, so the
 //    workgroups resident on one XCD share both activation rows and weight
 //    panels through its L2.
 //
@@ -83,10 +83,11 @@ constexpr int kCols = 256;              // tile columns (weight rows)
 constexpr int kStep = 128;              // bytes of K per step (64 bf16)
 constexpr int kStages = 4;              // A stages in LDS
 constexpr int kStage = kRows * kStep;   // 16 KB
-// row tiles per L2 group: 16 for the gated GEMM (12 column tiles per expert
-// here; 16 measured 1% faster than 8, 12 slower), 8 for the down GEMM (16
-// column tiles; 16 measured slower)
-constexpr int kGroupGated = 16, kGroupDown = 8;
+// row tiles per L2 group, measured on the skewed prefill (A/B runs on one
+// box): 16 for the gated GEMM (12 column tiles per expert there; 1% faster
+// than 8, while 12 and 32 were slower), 6 for the down GEMM (16 column tiles;
+// 1.6% faster than 8, 4 in between, 16 slower)
+constexpr int kGroupGated = 16, kGroupDown = 6;
 constexpr int kPrefetch = 2;            // fragments of the second sub-step read early
 
 #define MOE_LP(p) ((__attribute__((address_space(3))) void *)(p))

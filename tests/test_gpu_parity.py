@@ -228,10 +228,10 @@ SMALL = {
                                                            format=FORMAT_BATCHED, capacity=600,
                                                            logits_dist="normal"),
     # 128 x 256 MFMA tiles past one L2 group of row tiles (16 for the gated,
-    # 8 for the down GEMM): about 20 row tiles (a whole gated group and a
-    # partial one; two whole down groups and a partial one) x 2 column tiles,
-    # and about 33 row tiles (two whole gated groups, four whole down groups,
-    # and a partial one of each)
+    # 6 for the down GEMM): about 20 row tiles (a whole gated group and a
+    # partial one; three whole down groups and a partial one) x 2 column
+    # tiles, and about 33 row tiles (two whole gated groups, five whole down
+    # groups, and a partial one of each)
     "bf16_mfma_groups": WORKLOADS["mixtral_bf16"].replace(M=1200, K=512, I=256, E=4, topk=2, renormalize=False,
                                                           logits_dist="normal"),
     "bf16_mfma_18tiles": WORKLOADS["mixtral_bf16"].replace(M=2000, K=256, I=256, E=3, topk=2, renormalize=False,
