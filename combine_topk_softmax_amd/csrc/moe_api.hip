@@ -381,9 +381,10 @@ moe_status do_experts(const moe_problem &p, const void *a, const float *a_scale,
       MOE_HIP(launch_split_reduce(at<float>(ws, L.down_partial), (int)split, g2.split_stride, perm, L.perm_len,
                                   g2.n_pairs, (int)p.K, p.act_dtype, fused_out, s));
     }
-  } else if (streaming)
-    MOE_HIP(launch_stream_gemm(p.w_dtype, p.act_dtype, kGemmDown, g2, (int)(p.K / 128),
-                               stream_gemm_down_blocks(p.w_dtype, p.E, local_pairs, p.K, I), s));
+  } else if (streaming) {
+    const int nbw = stream_gemm_down_plan(p.w_dtype, p.E, local_pairs, p.K, I, &g2.bal_p, &g2.bal_h);
+    MOE_HIP(launch_stream_gemm(p.w_dtype, p.act_dtype, kGemmDown, g2, (int)(p.K / 128), nbw, s));
+  }
   else if (big)
     MOE_HIP(launch_mfma_gemm(kGemmDown, g2, mfma_gemm_n_tiles(kGemmDown, g2.Nw), s));
   else

@@ -237,6 +237,10 @@ struct GemmParams {
   // out + s * split_stride (out_perm unused); 0 or 1: no split
   int k_split;
   int64_t split_stride;
+  // streaming fp8 down GEMM, balanced plan (stream_gemm_down_plan): each row
+  // tile's columns form bal_h items of the wide width, then bal_p - bal_h of
+  // one block fewer per wavefront; 0: one width
+  int bal_p, bal_h;
   GemmTiles t;
 };
 
@@ -277,6 +281,9 @@ bool stream_gemm_fits(int w_dtype, int64_t K, int64_t I);
 // wide gated panels, 4), from the problem's shape: two when that still leaves
 // enough work items.
 int stream_gemm_down_blocks(int w_dtype, int64_t E, int64_t pairs, int64_t K, int64_t I);
+// blocks per wavefront of the down GEMM's (wide) items, and the balanced plan
+// if one is taken (bal_p = 0 otherwise)
+int stream_gemm_down_plan(int w_dtype, int64_t E, int64_t pairs, int64_t K, int64_t I, int *bal_p, int *bal_h);
 // K splits of the streaming down GEMM (1: none): bf16 shapes whose panels of
 // two weight blocks leave too few work items to fill the chip (few experts,
 // wide K) take two blocks per wavefront and split the reduction instead; the

@@ -21,7 +21,13 @@
 //    MFMA sits behind a branch (branches around memory operations make the
 //    compiler wait for every outstanding load);
 //  * work items are dealt out XCD by XCD: consecutive items of one expert land
-//    on the same XCD, so its activation rows stay in that XCD's L2.
+//    on the same XCD, so its activation rows stay in that XCD's L2;
+//  * the fp8 down GEMM can deal each row tile's output columns out as items of
+//    two widths (NBW and NBW - 1 blocks per wavefront), the wide ones first,
+//    so that every compute unit streams the same number of weight bytes where
+//    one width would leave the last round of items part-empty.  A column's
+//    arithmetic does not depend on the item that holds it, so the outputs are
+//    the same bits either way.
 //
 // MFMA: v_mfma_f32_16x16x32_bf16, or for fp8 v_mfma_scale_f32_16x16x128_f8f6f4
 // with unit block scales (OCP e4m3; the layer's fp32 block scales applied per
@@ -136,38 +142,68 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
   static_assert(!GATED || NBW == 2 || NBW == 4, "gated: 1 or 2 gate blocks per wavefront");
   constexpr int GB = GATED ? NBW / 2 : 1;
   static_assert(TMAX % 64 == 0 && TMAX <= 256, "row tile");
+  // the balanced down plan (fp8, 3 or 4 blocks per wavefront): items of NBW
+  // and NBW - 1 blocks
+  constexpr bool kBal = !GATED && kScaled && NBW >= 3;
 
   __shared__ __attribute__((aligned(16))) uint8_t As[2][TMAX * 128];
   __shared__ __attribute__((aligned(16))) float Sa[2][TMAX];
   __shared__ int32_t Orow[GATED ? 1 : TMAX];   // down: output row of each tile row
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int total = *g.t.tile_count * n_tiles;
+  const int tiles_n = *g.t.tile_count;
   const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
-  const int per = (total + 7) >> 3;
-  // An XCD's items past its last whole round (32 compute units), or all of
-  // them when there are fewer than a round, leave units idle; when they fill
-  // at most half a round, each of them becomes two work items over the two
-  // halves of its rows, adjacent so that the pair shares its weight panel
-  // through L2.  The outputs are the same: every row is computed as in the
-  // whole item (the fp8 epilogue's quantisation groups are per row).
-  const int whole = per & ~(kXcdUnits - 1), rem = per - whole;
-  const bool split_tail = MOE_STREAM_SPLIT_TAIL && GATED && rem <= kXcdUnits / 2;
-  int li = local, half = -1;
-  if (split_tail && local >= whole) {
-    li = whole + ((local - whole) >> 1);
-    half = (local - whole) & 1;
-  }
-  if (li >= per) return;
-  const int item = xcd * per + li;
-  if (item >= total) return;
-  // item -> (row tile c, K split sk, panel nt): the panels of one split are
-  // adjacent, so concurrent items share the split's activation K range
-  const int c = item / n_tiles;
   const int S = GATED || g.k_split <= 1 ? 1 : g.k_split;
-  const int n_panels = n_tiles / S;
-  const int sk = S > 1 ? (item - c * n_tiles) / n_panels : 0;
-  const int nt = item - c * n_tiles - sk * n_panels;
+  int c, sk = 0, nt = 0, half = -1;
+  int64_t col0 = 0;   // down: the item's first output column (weight row)
+  bool narrow = false;   // balanced down plan: the item holds NBW - 1 blocks per wavefront
+  if (kBal && g.bal_p > 0) {
+    // Balanced down plan: a row tile's K / 128 column units form bal_h items
+    // of NBW blocks per wavefront, then bal_p - bal_h items of NBW - 1; the
+    // wide items of all tiles come first, each group dealt out XCD by XCD.
+    const int n_wide = tiles_n * g.bal_h, n_narrow = tiles_n * (g.bal_p - g.bal_h);
+    const int per_wide = (n_wide + 7) >> 3;
+    if (local < per_wide) {
+      const int item = xcd * per_wide + local;
+      if (item >= n_wide) return;
+      c = item / g.bal_h;
+      col0 = (int64_t)(item - c * g.bal_h) * (128 * NBW);
+    } else {
+      const int per_narrow = (n_narrow + 7) >> 3, li = local - per_wide;
+      if (li >= per_narrow) return;
+      const int item = xcd * per_narrow + li, np = g.bal_p - g.bal_h;
+      if (item >= n_narrow) return;
+      c = item / np;
+      col0 = (int64_t)g.bal_h * (128 * NBW) + (int64_t)(item - c * np) * (128 * (NBW - 1));
+      narrow = true;
+    }
+  } else {
+    const int total = tiles_n * n_tiles;
+    const int per = (total + 7) >> 3;
+    // An XCD's items past its last whole round (32 compute units), or all of
+    // them when there are fewer than a round, leave units idle; when they fill
+    // at most half a round, each of them becomes two work items over the two
+    // halves of its rows, adjacent so that the pair shares its weight panel
+    // through L2.  The outputs are the same: every row is computed as in the
+    // whole item (the fp8 epilogue's quantisation groups are per row).
+    const int whole = per & ~(kXcdUnits - 1), rem = per - whole;
+    const bool split_tail = MOE_STREAM_SPLIT_TAIL && GATED && rem <= kXcdUnits / 2;
+    int li = local;
+    if (split_tail && local >= whole) {
+      li = whole + ((local - whole) >> 1);
+      half = (local - whole) & 1;
+    }
+    if (li >= per) return;
+    const int item = xcd * per + li;
+    if (item >= total) return;
+    // item -> (row tile c, K split sk, panel nt): the panels of one split are
+    // adjacent, so concurrent items share the split's activation K range
+    c = item / n_tiles;
+    const int n_panels = n_tiles / S;
+    sk = S > 1 ? (item - c * n_tiles) / n_panels : 0;
+    nt = item - c * n_tiles - sk * n_panels;
+    col0 = (int64_t)nt * (128 * NBW);
+  }
   const int32_t *tile = g.t.tiles + (int64_t)c * 4;
   const int e = tile[0];
   int64_t row0 = (int64_t)tile[1] + tile[2];
@@ -191,28 +227,9 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
   const int q = lane >> 4, r16 = lane & 15;
   const int64_t kblocks = g.Kred / 128;
 
-  // Weight rows of this wavefront: NBW blocks of 16 rows.  A lane reads two
-  // 16-byte pieces per block and K-step: bytes [32 q, 32 q + 32) of its row.
   const PackedGeom pg = packed_geom(g.Nw, row_bytes, GATED);
   const int64_t kstride = PACKED ? packed_kstep_stride(pg) : 128;   // bytes between K-steps
   constexpr int64_t pstride = PACKED ? 1024 : 16;                    // bytes between the two pieces
-  const uint8_t *wsrc[NBW];
-  const float *wscale[NBW];
-#pragma unroll
-  for (int b = 0; b < NBW; ++b) {
-    int64_t wrow0;
-    if (GATED)
-      wrow0 = (b >= GB ? g.half_n : 0) + (int64_t)nt * 128 * GB + wv * 16 * GB + (b % GB) * 16;
-    else
-      wrow0 = (int64_t)nt * (128 * NBW) + wv * (16 * NBW) + b * 16;
-    if (PACKED)
-      wsrc[b] = reinterpret_cast<const uint8_t *>(g.w) + packed_piece(pg, e, wrow0 + r16, 0, 2 * q) +
-                (int64_t)k0 * kstride;
-    else
-      wsrc[b] = reinterpret_cast<const uint8_t *>(g.w) + ((int64_t)e * g.Nw + wrow0 + r16) * row_bytes + q * 32 +
-                (int64_t)k0 * 128;
-    wscale[b] = kScaled ? g.w_scale + ((int64_t)e * (g.Nw / 128) + wrow0 / 128) * kblocks + k0 : nullptr;
-  }
   // A row (in the activation tensor) of tile row r.  Rows past the count map
   // to the last real row (so their loads share its cache lines) and padding
   // slots to row 0: an A row only feeds its own output row, which the
@@ -296,9 +313,28 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
     }
   };
 
-  // The main loop for NMB blocks of 16 rows (NMB * 16 >= T): every load, LDS
-  // access and MFMA is unconditional.
-  auto body = [&]<int NMB>() {
+  // The main loop for NMB blocks of 16 rows (NMB * 16 >= T) and NB weight
+  // blocks per wavefront: every load, LDS access and MFMA is unconditional.
+  auto body = [&]<int NMB, int NB>() {
+    // Weight rows of this wavefront: NB blocks of 16 rows.  A lane reads two
+    // 16-byte pieces per block and K-step: bytes [32 q, 32 q + 32) of its row.
+    const uint8_t *wsrc[NB];
+    const float *wscale[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      int64_t wrow0;
+      if (GATED)
+        wrow0 = (b >= GB ? g.half_n : 0) + (int64_t)nt * 128 * GB + wv * 16 * GB + (b % GB) * 16;
+      else
+        wrow0 = col0 + wv * (16 * NB) + b * 16;
+      if (PACKED)
+        wsrc[b] = reinterpret_cast<const uint8_t *>(g.w) + packed_piece(pg, e, wrow0 + r16, 0, 2 * q) +
+                  (int64_t)k0 * kstride;
+      else
+        wsrc[b] = reinterpret_cast<const uint8_t *>(g.w) + ((int64_t)e * g.Nw + wrow0 + r16) * row_bytes +
+                  q * 32 + (int64_t)k0 * 128;
+      wscale[b] = kScaled ? g.w_scale + ((int64_t)e * (g.Nw / 128) + wrow0 / 128) * kblocks + k0 : nullptr;
+    }
     constexpr int kPasses = (NMB * 16 + 63) / 64;   // A rows per thread per K-step
     int64_t arow[kPasses];
 #pragma unroll
@@ -323,11 +359,11 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
         if (tid < TMAX) Sa[st][tid] = rsa[j];
     };
 
-    u32x4 wb[D][NBW][2];
-    float wsv[D][NBW];
+    u32x4 wb[D][NB][2];
+    float wsv[D][NB];
     auto loadW = [&](int j, int ks) {
 #pragma unroll
-      for (int b = 0; b < NBW; ++b) {
+      for (int b = 0; b < NB; ++b) {
         const uint8_t *p = wsrc[b] + (int64_t)ks * kstride;
         wb[j][b][0] = load_w16<PACKED>(p);
         wb[j][b][1] = load_w16<PACKED>(p + pstride);
@@ -335,11 +371,11 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
       }
     };
 
-    f32x4 acc[NMB][NBW];
+    f32x4 acc[NMB][NB];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-      for (int b = 0; b < NBW; ++b) acc[mb][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int b = 0; b < NB; ++b) acc[mb][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     // One K-step of MFMAs from LDS stage st and weight registers j.
     auto compute = [&](int st, int j) {
@@ -362,7 +398,7 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
           }
           const int mb = x % NMB, t = x / NMB;
 #pragma unroll
-          for (int b = 0; b < NBW; ++b) acc[mb][b] = MM::mma(f[x], frag_at<frag>(wb[j][b], t), acc[mb][b]);
+          for (int b = 0; b < NB; ++b) acc[mb][b] = MM::mma(f[x], frag_at<frag>(wb[j][b], t), acc[mb][b]);
           // keep the read-ahead in place (the scheduler would otherwise move
           // each read next to its MFMAs and wait for it there)
           __builtin_amdgcn_sched_barrier(0);
@@ -376,12 +412,12 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
         static_assert(MM::kSteps == 1, "scaled path: one MFMA step per K-step");
         constexpr int kAhead = MOE_STREAM_FRAG_AHEAD < NMB ? MOE_STREAM_FRAG_AHEAD : NMB;
         frag f[NMB];
-        f32x4 part[2][NBW];
+        f32x4 part[2][NB];
 #pragma unroll
         for (int x = 0; x < kAhead; ++x) f[x] = lds_frag<frag>(A, x * 16 + r16, q * 32);
         auto issue = [&](int mb) {
 #pragma unroll
-          for (int b = 0; b < NBW; ++b)
+          for (int b = 0; b < NB; ++b)
             part[mb & 1][b] = MM::mma(f[mb], frag_at<frag>(wb[j][b], 0), f32x4{0.0f, 0.0f, 0.0f, 0.0f});
         };
         auto fold = [&](int mb) {
@@ -390,12 +426,12 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int b = 0; b < NBW; ++b) acc[mb][b][i] += part[mb & 1][b][i] * (sa[i] * wsv[j][b]);
+            for (int b = 0; b < NB; ++b) acc[mb][b][i] += part[mb & 1][b][i] * (sa[i] * wsv[j][b]);
           // Fold each block here: without this the compiler sinks all blocks'
           // scale FMAs to the end of the K-step and keeps every block's partial
           // sums live at once.
 #pragma unroll
-          for (int b = 0; b < NBW; ++b) asm volatile("" : "+v"(acc[mb][b]));
+          for (int b = 0; b < NB; ++b) asm volatile("" : "+v"(acc[mb][b]));
         };
         issue(0);
 #pragma unroll
@@ -460,7 +496,7 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
         // DeepSeek shapes).  Rows are staged in passes that fit the A buffers;
         // the 16-byte row padding spreads the 4 rows a store instruction
         // touches over different banks.
-        constexpr int kCols = GATED ? 128 * GB : 128 * NBW;
+        constexpr int kCols = GATED ? 128 * GB : 128 * NB;
         constexpr int kRowBytes = kCols * 2;
         constexpr int kPitch = kRowBytes + 16;
         constexpr int kFit = (2 * TMAX * 128 / kPitch) / 16 * 16;
@@ -468,7 +504,7 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
         constexpr int kChunks = kRowBytes / 16;
         static_assert(RP >= 16, "staging buffer holds at least one row block");
         uint8_t *stage = &As[0][0];
-        const int64_t col0 = (int64_t)nt * kCols;
+        const int64_t ocol0 = GATED ? (int64_t)nt * kCols : col0;
         __syncthreads();   // every wavefront is done reading the A tiles
 #pragma unroll
         for (int p0 = 0; p0 < NMB * 16; p0 += RP) {
@@ -485,8 +521,8 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
                 }
               } else {
 #pragma unroll
-                for (int b = 0; b < NBW; ++b)
-                  *reinterpret_cast<uint16_t *>(row + (wv * 16 * NBW + b * 16 + r16) * 2) =
+                for (int b = 0; b < NB; ++b)
+                  *reinterpret_cast<uint16_t *>(row + (wv * 16 * NB + b * 16 + r16) * 2) =
                       f32_to_bf16_bits(acc[mb][b][i]);
               }
             }
@@ -500,7 +536,7 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
               orow = Orow[p0 + rl];
               if (orow < 0) continue;
             }
-            *reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(out) + (orow * g.ldo + col0) * 2 + off) =
+            *reinterpret_cast<u32x4 *>(reinterpret_cast<uint8_t *>(out) + (orow * g.ldo + ocol0) * 2 + off) =
                 *reinterpret_cast<const u32x4 *>(stage + rl * kPitch + off);
           }
           __syncthreads();
@@ -528,8 +564,8 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
             const int64_t orow = Orow[r];
             if (orow < 0) continue;
 #pragma unroll
-            for (int b = 0; b < NBW; ++b) {
-              const int64_t col = (int64_t)nt * (128 * NBW) + wv * (16 * NBW) + b * 16 + r16;
+            for (int b = 0; b < NB; ++b) {
+              const int64_t col = col0 + wv * (16 * NB) + b * 16 + r16;
               if constexpr (OUT_BF16)
                 reinterpret_cast<uint16_t *>(out)[orow * g.ldo + col] = f32_to_bf16_bits(acc[mb][b][i]);
               else
@@ -552,26 +588,36 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
   // Row blocks rounded up to 1, 2, 4, 6, ... (one specialised loop each).
   const int nmb = (T + 15) >> 4;
   const int nq = nmb <= 1 ? 1 : (nmb + 1) & ~1;
-  switch (nq) {
-    case 1: body.template operator()<1>(); break;
-    case 2: body.template operator()<2>(); break;
-    case 4: body.template operator()<4>(); break;
-    case 6: body.template operator()<6>(); break;
-    case 8:
-      // four weight blocks per wavefront (wide fp8 panels) take tiles of at
-      // most 96 rows
-      if constexpr (NBW != 4) body.template operator()<8>();
-      break;
-    default:
-      if constexpr (TMAX >= 256) {
-        switch (nq) {
-          case 10: body.template operator()<10>(); break;
-          case 12: body.template operator()<12>(); break;
-          case 14: body.template operator()<14>(); break;
-          default: body.template operator()<16>(); break;
+  auto run = [&]<int NB>() {
+    switch (nq) {
+      case 1: body.template operator()<1, NB>(); break;
+      case 2: body.template operator()<2, NB>(); break;
+      case 4: body.template operator()<4, NB>(); break;
+      case 6: body.template operator()<6, NB>(); break;
+      case 8:
+        // four weight blocks per wavefront (wide fp8 panels) take tiles of at
+        // most 96 rows
+        if constexpr (NBW != 4) body.template operator()<8, NB>();
+        break;
+      default:
+        if constexpr (TMAX >= 256) {
+          switch (nq) {
+            case 10: body.template operator()<10, NB>(); break;
+            case 12: body.template operator()<12, NB>(); break;
+            case 14: body.template operator()<14, NB>(); break;
+            default: body.template operator()<16, NB>(); break;
+          }
         }
-      }
-      break;
+        break;
+    }
+  };
+  if constexpr (kBal) {
+    if (narrow)
+      run.template operator()<NBW - 1>();
+    else
+      run.template operator()<NBW>();
+  } else {
+    run.template operator()<NBW>();
   }
 }
 
@@ -580,7 +626,13 @@ hipError_t launch_cfg(int out_dtype, const GemmParams &g, int n_tiles, hipStream
   const int64_t items = (int64_t)g.t.max_tiles * n_tiles;
   // gated: room for a split tail (at most half a round more per XCD)
   const int64_t extra = MOE_STREAM_SPLIT_TAIL && GATED ? 8 * (kXcdUnits / 2) : 0;
-  dim3 grid((unsigned)(((items + 7) / 8) * 8 + extra)), block(kThreads);
+  int64_t blocks = ((items + 7) / 8) * 8 + extra;
+  if (!GATED && g.bal_p > 0) {
+    // balanced down plan: the wide items of every tile, then the narrow ones
+    const int64_t mt = g.t.max_tiles;
+    blocks = 8 * ((mt * g.bal_h + 7) / 8 + (mt * (g.bal_p - g.bal_h) + 7) / 8);
+  }
+  dim3 grid((unsigned)blocks), block(kThreads);
   const bool bf = out_dtype == MOE_DTYPE_BF16;
   if (g.w_packed) {
     if (bf)
@@ -710,6 +762,47 @@ int stream_gemm_down_blocks(int w_dtype, int64_t E, int64_t pairs, int64_t K, in
   return K % 256 == 0 && (I * eb / 128) % u2 == 0 && items >= 512 ? 2 : 1;
 }
 
+// Balanced fp8 down plan.  With one item width, the last round of items can
+// leave compute units idle (decode M=256: 448 items of 512 columns on 256
+// units, the second round three quarters full); these kernels stream at a
+// rate per unit, not per chip, so a part-empty round costs a whole one.  Each
+// row tile's K / 128 column units are then dealt out as bal_h items of w
+// blocks per wavefront and bal_p - bal_h items of w - 1 (w = 4 where the
+// uniform plan has 4, else 3), chosen so that the wide items fill whole rounds;
+// the plan is kept only where a model of the rounds (time per item: its
+// blocks plus a fixed quarter block for its prologue and epilogue) prefers it.
+// The expected tile count is one per expert with tokens; a different count on
+// the device changes the balance, not the result.
+#ifndef MOE_STREAM_DOWN_BALANCE
+#define MOE_STREAM_DOWN_BALANCE 1
+#endif
+#ifndef MOE_STREAM_DOWN3_D_FP8
+#define MOE_STREAM_DOWN3_D_FP8 2
+#endif
+int stream_gemm_down_plan(int w_dtype, int64_t E, int64_t pairs, int64_t K, int64_t I, int *bal_p, int *bal_h) {
+  *bal_p = *bal_h = 0;
+  const int nb0 = stream_gemm_down_blocks(w_dtype, E, pairs, K, I);
+  if (!MOE_STREAM_DOWN_BALANCE || w_dtype != MOE_DTYPE_FP8_E4M3 || nb0 < 2 || K % 128 != 0) return nb0;
+  const int w = nb0 == 4 ? 4 : 3;
+  if (w == 3 && (I / 128) % unroll_of(MOE_STREAM_DOWN3_D_FP8) != 0) return nb0;
+  const int64_t tiles = std::min(E, pairs), units = K / 128, cus = 8 * kXcdUnits;
+  if (tiles <= 0 || units % nb0 != 0) return nb0;
+  const double o = 0.25;
+  auto rounds = [&](int64_t n) { return (double)((n + cus - 1) / cus); };
+  double best = rounds(tiles * (units / nb0)) * (nb0 + o);
+  for (int64_t p = (units + w - 1) / w; p * (w - 1) <= units; ++p) {
+    const int64_t h = units - p * (w - 1);   // items of w blocks; p - h of w - 1
+    if (h <= 0 || h >= p || (tiles * h) % cus != 0) continue;
+    const double cost = rounds(tiles * h) * (w + o) + rounds(tiles * (p - h)) * (w - 1 + o);
+    if (cost < best - 1e-9) {
+      best = cost;
+      *bal_p = (int)p;
+      *bal_h = (int)h;
+    }
+  }
+  return *bal_p ? w : nb0;
+}
+
 #ifndef MOE_STREAM_DOWN_SPLIT
 #define MOE_STREAM_DOWN_SPLIT 2
 #endif
@@ -751,7 +844,13 @@ hipError_t launch_stream_gemm(int w_dtype, int out_dtype, GemmKind kind, const G
     return launch_cfg<2, false, 2, MOE_STREAM_DOWN2_D_BF16, 256>(MOE_DTYPE_F32, g, n_tiles / 2 * g.k_split, s);
   }
   // down: n_tiles = K / 128 from the caller, K / 256 with two blocks per
-  // wavefront, K / 512 with four (fp8)
+  // wavefront, K / 512 with four (fp8); the balanced plan sizes its own grid
+  if (g.bal_p > 0) {
+    if (!fp8 || g.bal_h <= 0 || g.bal_h >= g.bal_p) return hipErrorInvalidValue;
+    if (down_blocks == 4) return launch_cfg<1, false, 4, MOE_STREAM_DOWN4_D_FP8, 128>(out_dtype, g, 0, s);
+    if (down_blocks == 3) return launch_cfg<1, false, 3, MOE_STREAM_DOWN3_D_FP8, 128>(out_dtype, g, 0, s);
+    return hipErrorInvalidValue;
+  }
   if (down_blocks == 4 && fp8)
     return launch_cfg<1, false, 4, MOE_STREAM_DOWN4_D_FP8, 128>(out_dtype, g, n_tiles / 4, s);
   if (down_blocks == 2)

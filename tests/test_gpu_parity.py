@@ -253,6 +253,14 @@ SMALL = {
     # the same with K a multiple of 512: the down GEMM also takes four weight
     # blocks per wavefront (512 output columns per item)
     "fp8_wide_down4": WORKLOADS["decode_fp8_m64"].replace(M=192, K=512, I=2048, E=32, topk=8, capacity=192),
+    # fp8 down GEMM with two-block panels whose last round of items would be
+    # part-empty (32 experts x 20 panels = 640 items on 256 compute units):
+    # the balanced plan deals each row tile's 40 column units out as 8 items
+    # of three blocks per wavefront, then 8 of two; Zipf logits put up to 128
+    # rows on some experts (eight 16-row blocks) and none on others, so the
+    # device's tile count differs from the plan's expectation
+    "fp8_balanced_down": WORKLOADS["decode_fp8_m64"].replace(M=128, K=5120, I=256, E=32, topk=8, capacity=128,
+                                                             logits_dist="zipf"),
     # too few experts for a wide item per compute unit (an expert-parallel
     # shard's share): narrow panels
     "fp8_few_experts": WORKLOADS["decode_fp8_m64"].replace(M=96, K=256, I=256, E=4, topk=2, capacity=96),
