@@ -36,6 +36,7 @@
 // (F = 16 for bf16: two steps; F = 32 for fp8: one step).  A and B use the
 // same mapping, so the k permutation this implies cancels in the dot product.
 #include <algorithm>
+#include <utility>
 
 #include "moe_device.h"
 
@@ -469,7 +470,11 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
       if (tid < NMB * 16) Orow[tid] = orow_t;
     }
     __syncthreads();
-    for (int kb = 0; kb < nk; kb += U) {
+    // (the fp8 gated kernel with two blocks per wavefront keeps the plain
+    // loop for 6 and 8 row blocks, where the peeled steps spill registers)
+    constexpr bool kPeel = !(GATED && kScaled && NBW == 2 && NMB > 4);
+    int kb = 0;
+    for (; kb < (kPeel ? nk - U : nk); kb += U) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int k = kb + u;
@@ -479,6 +484,21 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
         storeA((u + 1) & 1, (u + 1) & 1);
         __syncthreads();
       }
+    }
+    // The last U K-steps issue no loads for steps past the end: loads still
+    // in flight when the loop ends would hold the epilogue at its first use of
+    // their registers until they land (about 2 us per item, measured).
+    auto last_step = [&]<int u>() {
+      if constexpr (u + 2 < U) loadA(u & 1, kb + u + 2);
+      compute(u & 1, u % D);
+      if constexpr (u + D < U) loadW(u % D, kb + u + D);
+      if constexpr (u + 1 < U) storeA((u + 1) & 1, (u + 1) & 1);
+      __syncthreads();
+    };
+    if constexpr (kPeel) {
+      [&]<int... us>(std::integer_sequence<int, us...>) {
+        (last_step.template operator()<us>(), ...);
+      }(std::make_integer_sequence<int, U>{});
     }
 
     // Epilogue: in a 16x16 block, lane holds column r16 of rows 4*q + i.  The
