@@ -275,34 +275,55 @@ __global__ __launch_bounds__(kThreads) void stream_gemm_kernel(const GemmParams 
       }
     }
     __syncthreads();
+    // The 16 lanes of a row group (same q) hold the same 4 * NMB rows: each
+    // lane works out the scale of one or two of them (two IEEE divisions per
+    // row, done once instead of in every lane), then every lane fetches the
+    // reciprocals of its rows from the lanes that computed them.
+    constexpr int kRowsQ = NMB * 4, kPer = (kRowsQ + 15) / 16;
+    float my_inv[kPer];
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) {
+      const int idx = t * 16 + r16, idc = min(idx, kRowsQ - 1);   // (mb, i) = (idc / 4, idc % 4)
+      const int r = (idc >> 2) * 16 + q * 4 + (idc & 3);
+      // the group's per-wavefront maxima are contiguous: 16-byte reads
+      float amax = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kGroupWaves; w += 4) {
+        const float4 m4 = *reinterpret_cast<const float4 *>(&rmax[r * 8 + grp * kGroupWaves + w]);
+        amax = fmaxf(amax, fmaxf(fmaxf(m4.x, m4.y), fmaxf(m4.z, m4.w)));
+      }
+      const float sc = group_scale(amax);
+      my_inv[t] = 1.0f / sc;
+      if (wv % kGroupWaves == 0 && idx < kRowsQ && r < T)
+        g.out_scale[(row0 + r) * (g.ldo / 128) + (int64_t)nt * GB + grp] = sc;
+    }
     float inv[NMB][4];
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
+    for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = mb * 16 + q * 4 + i;
-        // the group's per-wavefront maxima are contiguous: 16-byte reads
-        float amax = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kGroupWaves; w += 4) {
-          const float4 m4 = *reinterpret_cast<const float4 *>(&rmax[r * 8 + grp * kGroupWaves + w]);
-          amax = fmaxf(amax, fmaxf(fmaxf(m4.x, m4.y), fmaxf(m4.z, m4.w)));
-        }
-        const float sc = group_scale(amax);
-        inv[mb][i] = 1.0f / sc;
-        if (wv % kGroupWaves == 0 && r16 == 0 && r < T)
-          g.out_scale[(row0 + r) * (g.ldo / 128) + (int64_t)nt * GB + grp] = sc;
+        const int idx = mb * 4 + i;
+        inv[mb][i] = __shfl(my_inv[idx >> 4], q * 16 + (idx & 15), 64);
       }
-    }
     __syncthreads();   // the row maxima are read: their space takes the codes
+    // A row's consecutive codes sit in consecutive lanes: the first lane of
+    // each quad gathers its quad's four bytes (DPP quad permutes) and writes
+    // them as one 32-bit word, instead of four single-byte LDS writes.
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int gb = 0; gb < GB; ++gb)
-          codes[(mb * 16 + q * 4 + i) * kRowCodes + wv * 16 * GB + gb * 16 + r16] =
-              (uint8_t)quant_e4m3_inv(v[mb][gb][i], inv[mb][i]);
+        for (int gb = 0; gb < GB; ++gb) {
+          const int b = (int)quant_e4m3_inv(v[mb][gb][i], inv[mb][i]);
+          const int b1 = __builtin_amdgcn_update_dpp(0, b, 0x55, 0xF, 0xF, false);   // quad lane 1
+          const int b2 = __builtin_amdgcn_update_dpp(0, b, 0xAA, 0xF, 0xF, false);   // quad lane 2
+          const int b3 = __builtin_amdgcn_update_dpp(0, b, 0xFF, 0xF, 0xF, false);   // quad lane 3
+          if ((r16 & 3) == 0)
+            *reinterpret_cast<uint32_t *>(&codes[(mb * 16 + q * 4 + i) * kRowCodes + wv * 16 * GB + gb * 16 + r16]) =
+                (uint32_t)(b & 0xff) | ((uint32_t)(b1 & 0xff) << 8) | ((uint32_t)(b2 & 0xff) << 16) |
+                ((uint32_t)(b3 & 0xff) << 24);
+        }
     __syncthreads();
     // kRowCodes / 16 threads per row, 16 bytes each
     constexpr int kChunksRow = kRowCodes / 16;
